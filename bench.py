@@ -1,0 +1,242 @@
+"""Benchmark of the static FP8 gated-MLP hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of the gen-tower gated
+MLP workload (X [2048, 2048] BF16, gate/up [8192, 2048], down [2048, 8192]):
+
+  fp8_observe(X)        observer update (max) on the batch
+  gated_mlp_fp8(...)    quantize X once -> gate GEMM, up GEMM (FP8 MFMA,
+                        BF16 out) -> SwiGLU emitting FP8 -> down GEMM
+
+Inputs are seeded synthetic draws (mlp_fp8_quant_amd.workloads), resident in
+HBM before timing; weights are RTN-quantized and all static scales calibrated
+on the GPU with the library's own observer and quantize calls.
+
+Printed: one JSON line.  ``value`` is gated-MLP TFLOP/s (3 GEMMs, 2*M*N*K
+each, over the step time).  ``roofline`` is for the dominant kernel (the
+gate/up GEMM shape), with its average launch time measured with HIP events
+on the stream it runs on.  ``cpu_baseline`` times the CPU oracle on a row
+sample of the same workload (rank 0, N=1 only).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 gated-MLP TFLOP/s (+% of FP8 MFMA peak); quant/SwiGLU GB/s (% HBM)"
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+F16_PEAK_TFLOPS = 2500.0      # MI355X dense F16/BF16 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=2048,
+                   help="rows of X in the oracle's timed sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "the path has no multi-GPU code", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mlp_fp8_quant_amd as fp8
+    from mlp_fp8_quant_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    wl = workloads.gen_tower_mlp()
+    M, H = wl.x.shape
+    I = wl.weights["gate"].shape[0]
+
+    def dbf(b):
+        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = dbf(wl.x)
+    q, s = {}, {}
+    for k, w in wl.weights.items():
+        q[k], s[k] = fp8.rtn_weight(dbf(w))
+    st_x = fp8.new_observer_state(dev)
+    fp8.fp8_observe(x, st_x, fp8.OBS_MAX)
+    sx = fp8.fp8_scale_from_state(st_x)
+    qx = fp8.fp8_quant_static(x, sx)
+    G = fp8.fp8_linear(qx, q["gate"], sx, s["gate"])
+    U = fp8.fp8_linear(qx, q["up"], sx, s["up"])
+    st_h = fp8.new_observer_state(dev)
+    fp8.fp8_observe_swiglu(G, U, st_h, fp8.OBS_MAX)
+    sh = fp8.fp8_scale_from_state(st_h)
+    y = torch.empty_like(x)
+    ws = torch.empty(fp8.gated_mlp_fp8_workspace(M, H, I), dtype=torch.uint8, device=dev)
+    st_step = fp8.new_observer_state(dev)
+
+    def step(accum):
+        fp8.fp8_observe(x, st_step, fp8.OBS_MAX)
+        fp8.gated_mlp_fp8(x, sx, q["gate"], s["gate"], q["up"], s["up"], sh,
+                          q["down"], s["down"], out=y, workspace=ws, accum=accum)
+
+    def timed_steps(accum):
+        for _ in range(args.warmup):
+            step(accum)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            step(accum)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    gemm_flops = 2.0 * M * I * H * 3
+    ms_step = timed_steps(fp8.ACC_EXACT)
+    value = gemm_flops / (ms_step * 1e-3) / 1e12
+    ms_step_fp8 = timed_steps(fp8.ACC_FP8_MFMA)
+
+    # Per-kernel launch times: the composite's launch sequence issued as its
+    # five parts (bitwise the same kernels), HIP events between them, on the
+    # same stream.  Averaged over `steps` repetitions.
+    qxb = ws[:M * H].view(M, H)
+    Gb = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    Ub = torch.empty_like(Gb)
+    qh = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    names = ["quant", "gate", "up", "silu", "down"]
+
+    def per_kernel(accum):
+        # all repetitions are enqueued back to back (no host sync in between)
+        # so the GPU never idles waiting for a launch; events bracket each
+        # kernel on the stream it runs on
+        reps = max(args.steps, 10)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
+               for _ in range(reps + 2)]
+        for r in range(reps + 2):
+            ev = evs[r]
+            ev[0].record(stream)
+            fp8.fp8_quant_static(x, sx, out=qxb)
+            ev[1].record(stream)
+            fp8.fp8_linear(qxb, q["gate"], sx, s["gate"], out=Gb, accum=accum)
+            ev[2].record(stream)
+            fp8.fp8_linear(qxb, q["up"], sx, s["up"], out=Ub, accum=accum)
+            ev[3].record(stream)
+            fp8.silu_mul_2in_fp8(Gb, Ub, sh, out=qh)
+            ev[4].record(stream)
+            fp8.fp8_linear(qh, q["down"], sh, s["down"], out=y, accum=accum)
+            ev[5].record(stream)
+        torch.cuda.synchronize()
+        acc = {n: 0.0 for n in names}
+        for r in range(2, reps + 2):
+            for i, n in enumerate(names):
+                acc[n] += evs[r][i].elapsed_time(evs[r][i + 1])
+        return {n: acc[n] / reps * 1e3 for n in names}
+
+    us = per_kernel(fp8.ACC_EXACT)
+    us8 = per_kernel(fp8.ACC_FP8_MFMA)
+
+    gate_flops = 2.0 * M * I * H
+    gate_tflops = gate_flops / (us["gate"] * 1e-6) / 1e12
+    down_tflops = gate_flops / (us["down"] * 1e-6) / 1e12
+    quant_bytes = 3.0 * M * H
+    silu_bytes = 5.0 * M * I
+    kernels = {
+        "quant": {"us": us["quant"], "GB/s": quant_bytes / us["quant"] / 1e3,
+                  "bytes": quant_bytes},
+        "gate": {"us": us["gate"], "TFLOP/s": gate_tflops, "flops": gate_flops},
+        "up": {"us": us["up"], "TFLOP/s": gate_flops / (us["up"] * 1e-6) / 1e12},
+        "silu": {"us": us["silu"], "GB/s": silu_bytes / us["silu"] / 1e3,
+                 "bytes": silu_bytes},
+        "down": {"us": us["down"], "TFLOP/s": down_tflops},
+    }
+    for k in ("quant", "silu"):
+        kernels[k]["frac_hbm"] = kernels[k]["GB/s"] / HBM_PEAK_GBS
+
+    # the default engine runs on the F16 matrix cores (FP8 codes decoded
+    # exactly in the kernel): its peak is the dense F16 MFMA rate
+    roofline = {
+        "kernel": f"gemm (exact engine, f16 MFMA) {M}x{I}x{H} gate/up",
+        "bound": "mfma", "achieved": gate_tflops, "peak": F16_PEAK_TFLOPS,
+        "unit": "TFLOP/s", "frac": gate_tflops / F16_PEAK_TFLOPS,
+        "traffic": None,
+    }
+    g8 = gate_flops / (us8["gate"] * 1e-6) / 1e12
+    fp8_engine = {
+        "value": gemm_flops / (ms_step_fp8 * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "ms_per_step": ms_step_fp8,
+        "kernels_us": us8,
+        "roofline": {"kernel": f"gemm (fp8 MFMA engine) {M}x{I}x{H} gate/up",
+                     "bound": "mfma", "achieved": g8, "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": g8 / FP8_PEAK_TFLOPS},
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_rows)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": wl.name, "M": M, "H": H, "I": I,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "fp8_mfma_engine": fp8_engine,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(wl, rows):
+    """The oracle, as it stands, on a row sample of the same workload: the
+    whole chain (quantize X, exact gate/up GEMMs with the BF16 epilogue,
+    FP8 SwiGLU, exact down GEMM) for the first `rows` rows of X.  Reported
+    in the metric's unit: gated-MLP GEMM TFLOP/s of that sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import linear as olin
+    from oracle.swiglu import silu_mul_f64, silu_mul_fp8
+
+    x = wl.x[:rows]
+    q, s = {}, {}
+    for k, w in wl.weights.items():
+        q[k], s[k] = olin.rtn_weight(w)
+    sx = olin.scale_from_amax(olin.amax_f32(wl.x))
+    t = time.perf_counter()
+    qx = olin.quant_static(x, sx)
+    Sg, _ = olin.gemm_exact(qx, q["gate"])
+    Su, _ = olin.gemm_exact(qx, q["up"])
+    G = olin.epilogue_bf16(Sg, sx, s["gate"])
+    U = olin.epilogue_bf16(Su, sx, s["up"])
+    sh = olin.scale_from_amax(np.float32(np.max(np.abs(silu_mul_f64(G, U)))))
+    qh = silu_mul_fp8(G, U, sh).reshape(G.shape)
+    Sd, _ = olin.gemm_exact(qh, q["down"])
+    olin.epilogue_bf16(Sd, sh, s["down"])
+    dt = time.perf_counter() - t
+    H = x.shape[1]
+    I = q["gate"].shape[0]
+    flops = 2.0 * rows * I * H * 3
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": dt,
+            "sample": f"rows 0..{rows - 1} of X through the whole gated MLP "
+                      f"(M={rows}, H={H}, I={I}); float64 exact GEMMs"}
+
+
+if __name__ == "__main__":
+    main()

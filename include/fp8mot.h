@@ -1,0 +1,248 @@
+/*
+ * fp8mot.h -- C ABI of libfp8mot: the static per-tensor FP8 (OCP E4M3FN)
+ * W8A8 Linear stack of a Mixture-of-Transformers decoder tower, on AMD
+ * MI355X (gfx950).
+ *
+ * Sources (the passages each call follows are cited at the call):
+ *  [MC]  model card "Cosmos3-Nano-Policy-DROID, FP8 + RTN + moving-average
+ *        activation observer": header paragraph and section "Scheme".
+ *  [PR]  pull request "Load static FP8 Cosmos3 Nano/Super checkpoints without
+ *        re-quantizing them" (TensorRT-LLM 17476): sections "Description",
+ *        "What changed", "Supported surface, and what is refused", and the
+ *        commit messages.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    owned by the caller; the library allocates nothing and keeps no
+ *    per-call state.  Tensors are dense and contiguous (row-major); a
+ *    strided tensor must be rejected by the caller before it gets here
+ *    ([PR] first commit message: strided inputs are refused, not copied).
+ *  - BF16 tensors are passed as uint16_t bit patterns, FP8 tensors as uint8_t
+ *    E4M3FN codes (bias 7, no infinities, 0x7F/0xFF are NaN, max 448).
+ *  - Every scale is a `const float*` DEVICE pointer to one FP32 scalar.  The
+ *    library never reads a scale on the host: a host read would synchronize
+ *    the device on the hot path ([PR] "What changed": the shared-scale
+ *    invariant is checked at load, never in forward).  A NULL scale asks for
+ *    dynamic quantization, which the static path refuses
+ *    (FP8MOT_ERR_UNSUPPORTED; [PR] "What changed": dynamic quantization is
+ *    rejected explicitly).
+ *  - Scales must be finite and > 0; that is validated once at load with
+ *    fp8_check_shared_scale / by the caller, not per call.
+ *  - Calls are asynchronous on `stream`.  The return code covers argument
+ *    validation and kernel launch, not kernel completion.  Nothing is
+ *    launched when a call returns an error.
+ *  - Base pointers of tensors must be 16-byte aligned (128-bit loads and
+ *    stores); otherwise FP8MOT_ERR_MISALIGNED -- a refusal, not a slow path
+ *    ([PR] "Supported surface": a quiet fallback is worse than a refusal).
+ *  - Sizes are int64_t element counts.  Negative sizes are
+ *    FP8MOT_ERR_INVALID_ARG; an empty tensor (a zero size) is a valid no-op
+ *    and then data pointers may be NULL.
+ *  - Only gfx950 devices are supported; any other device gives
+ *    FP8MOT_ERR_UNSUPPORTED.
+ *  - The library is reentrant: calls on different streams may overlap.
+ */
+#ifndef FP8MOT_H
+#define FP8MOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8MOT_OK = 0,
+  FP8MOT_ERR_INVALID_ARG = 1,    /* NULL pointer, negative size, K % 16 != 0, bad enum, non-finite c */
+  FP8MOT_ERR_MISALIGNED = 2,     /* a tensor base pointer is not 16-byte aligned */
+  FP8MOT_ERR_SCALE_MISMATCH = 3, /* a shared-quantization group's input scales differ */
+  FP8MOT_ERR_UNSUPPORTED = 4,    /* NULL scale (dynamic quantization) or non-gfx950 device */
+  FP8MOT_ERR_HIP = 5,            /* a HIP runtime call or a kernel launch failed */
+  FP8MOT_ERR_WORKSPACE = 6       /* workspace NULL, misaligned or smaller than required */
+} fp8mot_status;
+
+/* Output kind of fp8_linear. */
+typedef enum {
+  FP8MOT_OUT_BF16 = 0, /* y = bf16_rne(acc * (s_x * s_w)), uint16_t [M, N] */
+  FP8MOT_OUT_FP8 = 1,  /* y = e4m3(acc * (s_x * s_w) / s_y), uint8_t [M, N] */
+  FP8MOT_OUT_F32 = 2   /* y = acc * (s_x * s_w) before any output rounding, float [M, N] */
+} fp8mot_out;
+
+/* Accumulation engine of the FP8 GEMMs (fp8_linear and the composites).
+ *
+ * FP8MOT_ACC_EXACT: the FP8 codes are decoded exactly to F16 in the kernel
+ *   and multiplied on the F16 matrix cores; products are accumulated to FP32
+ *   precision (|y - alpha*S| stays far inside 1e-5 * alpha * sum|terms|).
+ *   Peak is the F16 MFMA rate (2.5 PFLOP/s dense on MI355X).
+ * FP8MOT_ACC_FP8_MFMA: the native FP8 matrix-core instruction at twice that
+ *   rate.  On gfx950 the FP8 MFMA sums each group of 8 consecutive K products
+ *   on a grid 13 bits below the group's largest product (smaller products are
+ *   truncated toward zero) before adding the group to the FP32 accumulator;
+ *   the per-output error is bounded by alpha * sum over groups of
+ *   7 * 2^(e_max(group) - 13) and reaches ~1e-4 of sum|terms| on adversarial
+ *   inputs (about 5e-5 on Gaussian activations and weights).
+ * The two engines give different (each deterministic) results. */
+typedef enum {
+  FP8MOT_ACC_EXACT = 0,
+  FP8MOT_ACC_FP8_MFMA = 1
+} fp8mot_acc;
+
+/* Observer mode of fp8_observe. */
+typedef enum {
+  FP8MOT_OBS_MAX = 0,       /* running max of the per-call amax */
+  FP8MOT_OBS_MOVING_AVG = 1 /* moving average of the per-call amax */
+} fp8mot_obs;
+
+/* Observer state, 16 bytes in device memory.  An all-zero state is a fresh
+ * observer (the caller zero-fills it once).  `m` is the observed value,
+ * `count` the number of calls folded in; `pending` is the library's own
+ * reduction slot and is left at zero after each fp8_observe. */
+typedef struct {
+  float m;
+  int32_t count;
+  uint32_t pending;
+  uint32_t reserved;
+} fp8mot_observer_state;
+
+/* ------------------------------------------------------------------ */
+/* Library                                                             */
+/* ------------------------------------------------------------------ */
+
+/* Checks that `device` is a gfx950 GPU and caches that result.  Optional:
+ * every call checks the current device itself.  Returns FP8MOT_OK,
+ * FP8MOT_ERR_UNSUPPORTED (other architecture) or FP8MOT_ERR_HIP. */
+int fp8mot_init(int device);
+
+/* Static message for a status code (never NULL). */
+const char* fp8mot_status_string(int status);
+
+/* Number of activation-quantization launches made by this process so far
+ * (fp8_quant_static, and the one inside each composite).  A test hook for
+ * the single-quantization property: a composite call adds exactly 1. */
+uint64_t fp8mot_debug_quant_launches(void);
+
+/* ------------------------------------------------------------------ */
+/* Steps of the hot path                                               */
+/* ------------------------------------------------------------------ */
+
+/* Static activation quantization ([MC] "Scheme": FP8 E4M3 activations with
+ * one static per-tensor scale; [PR] "What changed": the shared activation is
+ * quantized once and the FP8 tensor is handed to every projection).
+ *   q[i] = e4m3(fp32(x[i]) / *d_scale)
+ * with one correctly rounded FP32 division and round-to-nearest-even E4M3
+ * encoding that saturates to +-448 (NaN -> 0x7F, the sign of zero kept).
+ * x: BF16 [n], q: E4M3 [n] (flat; any rank). */
+int fp8_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
+                     const float* d_scale, hipStream_t stream);
+
+/* FP8 Linear, one projection with its own weight and weight scale
+ * ([PR] "Description": each projection keeps s_i * qW_i, no re-quantization
+ * onto max(s); commit messages: each Linear applies its own scale in the
+ * GEMM epilogue).
+ *   acc[m,n] = sum_k e4m3_value(qx[m,k]) * e4m3_value(qw[n,k])  (FP32 accumulation)
+ *   alpha    = fp32(*d_sx * *d_sw)
+ *   y[m,n]   = per `out_kind` (see fp8mot_out), acc * alpha first.
+ * qx: E4M3 [M, K] row-major; qw: E4M3 [N, K] row-major (out x in, K
+ * contiguous); y: [M, N] row-major, contiguous (leading dimension N).
+ * K must be a multiple of 16.  d_sy is used only for FP8MOT_OUT_FP8 (NULL
+ * there is FP8MOT_ERR_UNSUPPORTED) and ignored otherwise.  K == 0 writes
+ * zeros.  `accum` selects the engine (fp8mot_acc). */
+int fp8_linear(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
+               int64_t N, int64_t K, const float* d_sx, const float* d_sw,
+               int out_kind, const float* d_sy, int accum, hipStream_t stream);
+
+/* Two-input SwiGLU with direct FP8 emission ([PR] "What changed" and the
+ * first commit message: SiLU(G) * U from two separate tensors, quantized for
+ * the FP8 down projection; flat indexing, rank-agnostic).
+ *   q[i] = e4m3(silu(g[i]) * u[i] / *d_s_out),  silu(g) = g / (1 + exp(-g))
+ * evaluated in FP32.  g, u: BF16 [n]; q: E4M3 [n]. */
+int silu_mul_2in_fp8(const uint16_t* g, const uint16_t* u, uint8_t* q,
+                     int64_t n, const float* d_s_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* Composites (one shared quantization, contiguous outputs, no sync)   */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of workspace gated_mlp_fp8 needs: qX [M,H] + G, U [M,I] BF16 + qH
+ * [M,I], each region 256-byte aligned.  Returns 0 for negative sizes. */
+size_t gated_mlp_fp8_workspace(int64_t M, int64_t H, int64_t I);
+
+/* Gated MLP with split gate/up ([PR] "What changed": GatedMLP with
+ * split_gate_up quantizes the shared activation once and hands both
+ * projections the FP8 tensor; SiLU(G)*U emits FP8 at the down input scale).
+ *   qX = quant(x; sx); G = linear(qX, wg; sx, sg); U = linear(qX, wu; sx, su)
+ *   qH = silu_mul_2in(G, U; sh); y = linear(qH, wd; sh, sd)  (BF16 out)
+ * Bitwise equal to those five calls.  x: [M, H]; wg, wu: [I, H]; wd: [H, I];
+ * y: [M, H].  H and I multiples of 16.  ws: device workspace of at least
+ * gated_mlp_fp8_workspace(M, H, I) bytes, 256-byte aligned.  `accum`
+ * selects the GEMM engine (fp8mot_acc) of all three GEMMs. */
+int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                  const float* d_sx, const uint8_t* wg, const float* d_sg,
+                  const uint8_t* wu, const float* d_su, const float* d_sh,
+                  const uint8_t* wd, const float* d_sd, uint16_t* y, void* ws,
+                  size_t ws_bytes, int accum, hipStream_t stream);
+
+/* Bytes of workspace qkv_fp8 needs: qX [M, H], 256-byte aligned. */
+size_t qkv_fp8_workspace(int64_t M, int64_t H);
+
+/* Split Q/K/V with one shared activation quantization ([PR] "What changed":
+ * Attention with share_qkv_input_quant; "It is also faster": split
+ * projections give contiguous outputs).
+ *   qX = quant(x; sx); yq = linear(qX, wq; sx, sq); yk = ...; yv = ...
+ * x: [M, H]; wq: [Nq, H]; wk: [Nk, H]; wv: [Nv, H]; yq: [M, Nq], yk: [M, Nk],
+ * yv: [M, Nv], three separate contiguous BF16 tensors.  H multiple of 16.
+ * Cross-attention, where k/v read a different tensor than q, must not use
+ * this call: quantize each input separately and use fp8_linear.  `accum`
+ * selects the GEMM engine (fp8mot_acc). */
+int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
+            const uint8_t* wq, int64_t Nq, const float* d_sq,
+            const uint8_t* wk, int64_t Nk, const float* d_sk,
+            const uint8_t* wv, int64_t Nv, const float* d_sv, uint16_t* yq,
+            uint16_t* yk, uint16_t* yv, void* ws, size_t ws_bytes, int accum,
+            hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
+/* Calibration                                                         */
+/* ------------------------------------------------------------------ */
+
+/* Folds one calibration call into an observer ([MC] header and "Scheme":
+ * static input scales from the global max of the activations, or from a
+ * moving average of the per-call maxima with constant 0.01).
+ *   a = max |x[i]|   (NaN if any x[i] is NaN)
+ *   first call: m = a
+ *   FP8MOT_OBS_MAX:        m = max(m, a)            (NaN propagates)
+ *   FP8MOT_OBS_MOVING_AVG: m = m + c * (a - m)      (three FP32 roundings, no FMA)
+ * x: BF16 [n], n >= 1.  d_state: device fp8mot_observer_state (zero-filled
+ * before the first call; 16-byte aligned).  `c` is used by the moving
+ * average only and must be finite.  Calls on one state must be
+ * stream-ordered. */
+int fp8_observe(const uint16_t* x, int64_t n, void* d_state, int mode,
+                float c, hipStream_t stream);
+
+/* Same as fp8_observe with a = max |silu(g[i]) * u[i]| (FP32 evaluation as in
+ * silu_mul_2in_fp8): calibrates the down projection's input scale from the
+ * gate/up outputs without materializing the product. */
+int fp8_observe_swiglu(const uint16_t* g, const uint16_t* u, int64_t n,
+                       void* d_state, int mode, float c, hipStream_t stream);
+
+/* *d_scale = fp32(state.m / 448): the static per-tensor scale. */
+int fp8_scale_from_state(const void* d_state, float* d_scale,
+                         hipStream_t stream);
+
+/* Load-time check of a shared-quantization group ([PR] "What changed": the
+ * projections sharing one quantized activation must carry the same
+ * calibrated input_scale; checked at load, never in forward).
+ * h_scales: HOST array of n >= 1 scales.  FP8MOT_OK iff all are finite,
+ * > 0 and bitwise equal; FP8MOT_ERR_SCALE_MISMATCH if they differ;
+ * FP8MOT_ERR_INVALID_ARG for NULL, n < 1, or a non-finite or non-positive
+ * scale.  Pure host code: usable without a GPU. */
+int fp8_check_shared_scale(const float* h_scales, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MOT_H */

@@ -1,1 +1,16 @@
-"""Static per-tensor FP8 (E4M3) W8A8 Linear stack for AMD MI355X (gfx950)."""
+"""Static per-tensor FP8 (OCP E4M3FN) W8A8 Linear stack for AMD MI355X.
+
+The compute lives in ``libfp8mot.so`` (HIP kernels for gfx950 behind a C
+ABI, declared in ``include/fp8mot.h``); ``mlp_fp8_quant_amd.api`` is the thin
+PyTorch binding with the same names.  The library is loaded on first use and
+its absence is an error -- there is no CPU path.
+"""
+
+from .api import (ACC_EXACT, ACC_FP8_MFMA, OBS_MAX,  # noqa: F401
+                  OBS_MOVING_AVG, OUT_BF16, OUT_F32,
+                  OUT_FP8, Fp8motError, debug_quant_launches,
+                  fp8_check_shared_scale, fp8_linear, fp8_observe,
+                  fp8_observe_swiglu, fp8_quant_static, fp8_scale_from_state,
+                  gated_mlp_fp8, gated_mlp_fp8_workspace, init,
+                  new_observer_state, qkv_fp8, qkv_fp8_workspace, rtn_weight,
+                  silu_mul_2in_fp8)

@@ -1,0 +1,251 @@
+"""PyTorch-facing binding of libfp8mot: same names as the C ABI.
+
+Torch provides device memory and the current stream; every computation runs
+in libfp8mot's HIP kernels.  Each wrapper checks dtype, device and
+contiguity and refuses anything else (a strided tensor is rejected, never
+copied), flattens rank-N ``[..., H]`` activations to ``[M, H]``, and maps a
+non-OK status to ``Fp8motError``.
+
+Dtypes at this boundary: BF16 tensors are ``torch.bfloat16``; FP8 tensors
+are ``torch.uint8`` holding E4M3FN codes; scales are one-element
+``torch.float32`` device tensors.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import Fp8motError  # noqa: F401
+
+OUT_BF16, OUT_FP8, OUT_F32 = 0, 1, 2
+ACC_EXACT, ACC_FP8_MFMA = 0, 1
+OBS_MAX, OBS_MOVING_AVG = 0, 1
+_OUT_DTYPE = {OUT_BF16: torch.bfloat16, OUT_FP8: torch.uint8, OUT_F32: torch.float32}
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, name, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (strided tensors are refused)")
+
+
+def _scale(t, name, device):
+    if t is None:
+        return None  # the library refuses a NULL scale (dynamic quantization)
+    _need(t, name, torch.float32, device)
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold exactly one float32")
+    return t
+
+
+def fp8_quant_static(x, scale, out=None):
+    """E4M3 codes of BF16 ``x`` at the static per-tensor ``scale``."""
+    _need(x, "x", torch.bfloat16)
+    _scale(scale, "scale", x.device)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _need(out, "out", torch.uint8, x.device)
+    if out.numel() != x.numel():
+        raise ValueError("out must have as many elements as x")
+    _lib.call("fp8_quant_static", _ptr(x), _ptr(out), x.numel(), _ptr(scale),
+              _stream(x))
+    return out
+
+
+def fp8_linear(qx, qw, sx, sw, out_kind=OUT_BF16, sy=None, out=None,
+               accum=ACC_EXACT):
+    """y = (qx . qw^T) * (sx * sw) with qx [..., K] and qw [N, K] E4M3.
+
+    ``accum``: ACC_EXACT (F16 matrix cores on exactly decoded codes, FP32-grade
+    accumulation) or ACC_FP8_MFMA (native FP8 matrix cores, 2x the rate, with
+    the hardware's 8-product windowed accumulation)."""
+    _need(qx, "qx", torch.uint8)
+    _need(qw, "qw", torch.uint8, qx.device)
+    if qw.dim() != 2 or qx.dim() < 1 or qx.shape[-1] != qw.shape[1]:
+        raise ValueError("shapes: qx [..., K], qw [N, K]")
+    _scale(sx, "sx", qx.device)
+    _scale(sw, "sw", qx.device)
+    _scale(sy, "sy", qx.device)
+    K = qw.shape[1]
+    N = qw.shape[0]
+    M = math.prod(qx.shape[:-1])
+    if out is None:
+        out = torch.empty((*qx.shape[:-1], N), dtype=_OUT_DTYPE[out_kind],
+                          device=qx.device)
+    _need(out, "out", _OUT_DTYPE[out_kind], qx.device)
+    if out.numel() != M * N:
+        raise ValueError("out must hold M * N elements")
+    _lib.call("fp8_linear", _ptr(qx), _ptr(qw), _ptr(out), M, N, K, _ptr(sx),
+              _ptr(sw), out_kind, _ptr(sy), accum, _stream(qx))
+    return out
+
+
+def silu_mul_2in_fp8(g, u, s_out, out=None):
+    """E4M3 codes of silu(g) * u at ``s_out``; g and u BF16 of equal shape."""
+    _need(g, "g", torch.bfloat16)
+    _need(u, "u", torch.bfloat16, g.device)
+    if g.shape != u.shape:
+        raise ValueError("g and u must have the same shape")
+    _scale(s_out, "s_out", g.device)
+    if out is None:
+        out = torch.empty(g.shape, dtype=torch.uint8, device=g.device)
+    _need(out, "out", torch.uint8, g.device)
+    if out.numel() != g.numel():
+        raise ValueError("out must have as many elements as g")
+    _lib.call("silu_mul_2in_fp8", _ptr(g), _ptr(u), _ptr(out), g.numel(),
+              _ptr(s_out), _stream(g))
+    return out
+
+
+def gated_mlp_fp8_workspace(M, H, I):
+    return int(_lib.lib().gated_mlp_fp8_workspace(M, H, I))
+
+
+def _workspace(nbytes, device, ws):
+    if ws is None:
+        # 256-byte aligned: the caching allocator aligns blocks to 512 bytes
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _need(ws, "workspace", torch.uint8, device)
+    return ws
+
+
+def gated_mlp_fp8(x, sx, wg, sg, wu, su, sh, wd, sd, out=None, workspace=None,
+                  accum=ACC_EXACT):
+    """Split gate/up gated MLP; x [..., H] BF16 -> y [..., H] BF16."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    for t, n in ((wg, "wg"), (wu, "wu"), (wd, "wd")):
+        _need(t, n, torch.uint8, dev)
+    H = x.shape[-1]
+    I = wg.shape[0]
+    if wg.shape != (I, H) or wu.shape != (I, H) or wd.shape != (H, I):
+        raise ValueError("shapes: wg, wu [I, H]; wd [H, I]")
+    for t, n in ((sx, "sx"), (sg, "sg"), (su, "su"), (sh, "sh"), (sd, "sd")):
+        _scale(t, n, dev)
+    M = math.prod(x.shape[:-1])
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    if out.numel() != M * H:
+        raise ValueError("out must hold M * H elements")
+    nb = gated_mlp_fp8_workspace(M, H, I)
+    ws = _workspace(nb, dev, workspace)
+    _lib.call("gated_mlp_fp8", _ptr(x), M, H, I, _ptr(sx), _ptr(wg), _ptr(sg),
+              _ptr(wu), _ptr(su), _ptr(sh), _ptr(wd), _ptr(sd), _ptr(out),
+              _ptr(ws), ws.numel(), accum, _stream(x))
+    return out
+
+
+def qkv_fp8_workspace(M, H):
+    return int(_lib.lib().qkv_fp8_workspace(M, H))
+
+
+def qkv_fp8(x, sx, wq, sq, wk, sk, wv, sv, outs=None, workspace=None,
+            accum=ACC_EXACT):
+    """Split Q/K/V over one shared quantization; returns (yq, yk, yv)."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    H = x.shape[-1]
+    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv")):
+        _need(t, n, torch.uint8, dev)
+        if t.dim() != 2 or t.shape[1] != H:
+            raise ValueError(f"{n} must be [N, H]")
+    for t, n in ((sx, "sx"), (sq, "sq"), (sk, "sk"), (sv, "sv")):
+        _scale(t, n, dev)
+    M = math.prod(x.shape[:-1])
+    if outs is None:
+        outs = tuple(torch.empty((*x.shape[:-1], w.shape[0]), dtype=torch.bfloat16,
+                                 device=dev) for w in (wq, wk, wv))
+    for o, w, n in zip(outs, (wq, wk, wv), ("yq", "yk", "yv")):
+        _need(o, n, torch.bfloat16, dev)
+        if o.numel() != M * w.shape[0]:
+            raise ValueError(f"{n} must hold M * N elements")
+    ws = _workspace(qkv_fp8_workspace(M, H), dev, workspace)
+    yq, yk, yv = outs
+    _lib.call("qkv_fp8", _ptr(x), M, H, _ptr(sx), _ptr(wq), wq.shape[0],
+              _ptr(sq), _ptr(wk), wk.shape[0], _ptr(sk), _ptr(wv), wv.shape[0],
+              _ptr(sv), _ptr(yq), _ptr(yk), _ptr(yv), _ptr(ws), ws.numel(),
+              accum, _stream(x))
+    return yq, yk, yv
+
+
+def new_observer_state(device):
+    """A fresh (zero-filled) 16-byte observer state on ``device``."""
+    return torch.zeros(4, dtype=torch.int32, device=device)
+
+
+def fp8_observe(x, state, mode=OBS_MAX, c=0.01):
+    """Fold amax(|x|) of one calibration call into ``state``."""
+    _need(x, "x", torch.bfloat16)
+    _need(state, "state", torch.int32, x.device)
+    if state.numel() != 4:
+        raise ValueError("state must be a 16-byte observer state")
+    _lib.call("fp8_observe", _ptr(x), x.numel(), _ptr(state), mode, c,
+              _stream(x))
+    return state
+
+
+def fp8_observe_swiglu(g, u, state, mode=OBS_MAX, c=0.01):
+    """Fold amax(|silu(g) * u|) into ``state``."""
+    _need(g, "g", torch.bfloat16)
+    _need(u, "u", torch.bfloat16, g.device)
+    if g.shape != u.shape:
+        raise ValueError("g and u must have the same shape")
+    _need(state, "state", torch.int32, g.device)
+    if state.numel() != 4:
+        raise ValueError("state must be a 16-byte observer state")
+    _lib.call("fp8_observe_swiglu", _ptr(g), _ptr(u), g.numel(), _ptr(state),
+              mode, c, _stream(g))
+    return state
+
+
+def fp8_scale_from_state(state, out=None):
+    """Static scale m / 448 from an observer state (one float32 on device)."""
+    _need(state, "state", torch.int32)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=state.device)
+    _need(out, "out", torch.float32, state.device)
+    _lib.call("fp8_scale_from_state", _ptr(state), _ptr(out), _stream(state))
+    return out
+
+
+def fp8_check_shared_scale(scales):
+    """Load-time check: raises Fp8motError unless all scales are equal,
+    finite and > 0.  ``scales`` is a host sequence of floats."""
+    n = len(scales)
+    arr = (ctypes.c_float * max(n, 1))(*[float(s) for s in scales])
+    _lib.call("fp8_check_shared_scale", arr, n)
+
+
+def debug_quant_launches():
+    return int(_lib.lib().fp8mot_debug_quant_launches())
+
+
+def init(device=0):
+    _lib.call("fp8mot_init", int(device))
+
+
+def rtn_weight(w, state=None):
+    """RTN per-tensor E4M3 weight with scale amax/448, on the GPU:
+    fp8_observe (max) -> fp8_scale_from_state -> fp8_quant_static."""
+    st = new_observer_state(w.device)
+    fp8_observe(w, st, OBS_MAX)
+    s = fp8_scale_from_state(st)
+    return fp8_quant_static(w, s), s

@@ -1,0 +1,288 @@
+// C ABI of libfp8mot (declared in include/fp8mot.h): argument validation,
+// device checks, workspace layout and the composites.  Every step of the
+// path runs in this library's kernels; validation happens before any HIP
+// call, so a refused call launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/fp8mot.h"
+#include "kernels.h"
+
+using namespace fp8mot;
+
+namespace {
+
+std::atomic<uint64_t> g_quant_launches{0};
+
+constexpr int kMaxDevices = 64;
+// per device: 0 = not checked, 1 = gfx950, 2 = unsupported
+std::atomic<int> g_dev_state[kMaxDevices];
+std::atomic<int> g_dev_cus[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+int check_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return FP8MOT_ERR_UNSUPPORTED;
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8MOT_ERR_HIP;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    st = ok ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? FP8MOT_OK : FP8MOT_ERR_UNSUPPORTED;
+}
+
+// Checks the current device; on success stores its CU count.
+int current_device(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8MOT_ERR_HIP;
+  const int st = check_device(dev);
+  if (st == FP8MOT_OK) *cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+  return st;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8MOT_OK : FP8MOT_ERR_HIP; }
+
+// Blocks for the grid-stride elementwise kernels: 8 workgroups per CU.
+int ew_blocks(int cus) { return cus * 8; }
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct MlpLayout {
+  size_t qx, g, u, qh, total;
+};
+
+MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I) {
+  MlpLayout l;
+  l.qx = 0;
+  l.g = l.qx + round256((size_t)M * H);
+  l.u = l.g + round256((size_t)M * I * 2);
+  l.qh = l.u + round256((size_t)M * I * 2);
+  l.total = l.qh + round256((size_t)M * I);
+  return l;
+}
+
+// Validation shared by the GEMM entry points.
+int check_linear(const uint8_t* qx, const uint8_t* qw, const void* y, int64_t M,
+                 int64_t N, int64_t K, const float* sx, const float* sw,
+                 int out_kind, const float* sy, int accum) {
+  if (out_kind < 0 || out_kind > 2) return FP8MOT_ERR_INVALID_ARG;
+  if (accum != FP8MOT_ACC_EXACT && accum != FP8MOT_ACC_FP8_MFMA) return FP8MOT_ERR_INVALID_ARG;
+  if (sx == nullptr || sw == nullptr) return FP8MOT_ERR_UNSUPPORTED;
+  if (out_kind == FP8MOT_OUT_FP8 && sy == nullptr) return FP8MOT_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || (K % 16) != 0) return FP8MOT_ERR_INVALID_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8MOT_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FP8MOT_OK;
+  if (y == nullptr || (K > 0 && (qx == nullptr || qw == nullptr)))
+    return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(y) || !aligned16(qx) || !aligned16(qw)) return FP8MOT_ERR_MISALIGNED;
+  return FP8MOT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8mot_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return FP8MOT_ERR_INVALID_ARG;
+  return check_device(device);
+}
+
+const char* fp8mot_status_string(int status) {
+  switch (status) {
+    case FP8MOT_OK: return "ok";
+    case FP8MOT_ERR_INVALID_ARG: return "invalid argument (NULL pointer, negative size, K % 16 != 0, bad enum or non-finite constant)";
+    case FP8MOT_ERR_MISALIGNED: return "tensor base pointer not 16-byte aligned";
+    case FP8MOT_ERR_SCALE_MISMATCH: return "input scales of a shared-quantization group differ";
+    case FP8MOT_ERR_UNSUPPORTED: return "unsupported: NULL scale (dynamic quantization) or non-gfx950 device";
+    case FP8MOT_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case FP8MOT_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
+    default: return "unknown status";
+  }
+}
+
+uint64_t fp8mot_debug_quant_launches(void) { return g_quant_launches.load(); }
+
+int fp8_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
+                     const float* d_scale, hipStream_t stream) {
+  if (d_scale == nullptr) return FP8MOT_ERR_UNSUPPORTED;
+  if (n < 0) return FP8MOT_ERR_INVALID_ARG;
+  if (n == 0) return FP8MOT_OK;
+  if (x == nullptr || q == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(q)) return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  g_quant_launches.fetch_add(1);
+  return hip_status(launch_quant_static(x, q, n, d_scale, ew_blocks(cus), stream));
+}
+
+int fp8_linear(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
+               int64_t N, int64_t K, const float* d_sx, const float* d_sw,
+               int out_kind, const float* d_sy, int accum, hipStream_t stream) {
+  int st = check_linear(qx, qw, y, M, N, K, d_sx, d_sw, out_kind, d_sy, accum);
+  if (st != FP8MOT_OK || M == 0 || N == 0) return st;
+  int cus = 0;
+  st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_gemm(qx, qw, y, M, N, K, d_sx, d_sw, out_kind, d_sy, accum, cus, stream));
+}
+
+int silu_mul_2in_fp8(const uint16_t* g, const uint16_t* u, uint8_t* q,
+                     int64_t n, const float* d_s_out, hipStream_t stream) {
+  if (d_s_out == nullptr) return FP8MOT_ERR_UNSUPPORTED;
+  if (n < 0) return FP8MOT_ERR_INVALID_ARG;
+  if (n == 0) return FP8MOT_OK;
+  if (g == nullptr || u == nullptr || q == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(g) || !aligned16(u) || !aligned16(q)) return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_silu_mul(g, u, q, n, d_s_out, ew_blocks(cus), stream));
+}
+
+size_t gated_mlp_fp8_workspace(int64_t M, int64_t H, int64_t I) {
+  if (M < 0 || H < 0 || I < 0) return 0;
+  return mlp_layout(M, H, I).total;
+}
+
+int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                  const float* d_sx, const uint8_t* wg, const float* d_sg,
+                  const uint8_t* wu, const float* d_su, const float* d_sh,
+                  const uint8_t* wd, const float* d_sd, uint16_t* y, void* ws,
+                  size_t ws_bytes, int accum, hipStream_t stream) {
+  if (!d_sx || !d_sg || !d_su || !d_sh || !d_sd) return FP8MOT_ERR_UNSUPPORTED;
+  if (accum != FP8MOT_ACC_EXACT && accum != FP8MOT_ACC_FP8_MFMA) return FP8MOT_ERR_INVALID_ARG;
+  if (M < 0 || H < 0 || I < 0 || (H % 16) != 0 || (I % 16) != 0)
+    return FP8MOT_ERR_INVALID_ARG;
+  if (M > INT32_MAX || H > INT32_MAX || I > INT32_MAX) return FP8MOT_ERR_INVALID_ARG;
+  if (M == 0 || H == 0) return FP8MOT_OK;
+  if (!x || !wg || !wu || !wd || !y) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(y))
+    return FP8MOT_ERR_MISALIGNED;
+  const MlpLayout l = mlp_layout(M, H, I);
+  if (ws == nullptr || !aligned256(ws) || ws_bytes < l.total) return FP8MOT_ERR_WORKSPACE;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* qx = base + l.qx;
+  uint16_t* g = reinterpret_cast<uint16_t*>(base + l.g);
+  uint16_t* u = reinterpret_cast<uint16_t*>(base + l.u);
+  uint8_t* qh = base + l.qh;
+  g_quant_launches.fetch_add(1);
+  hipError_t e = launch_quant_static(x, qx, M * H, d_sx, ew_blocks(cus), stream);
+  if (e == hipSuccess && I > 0)
+    e = launch_gemm(qx, wg, g, M, I, H, d_sx, d_sg, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
+  if (e == hipSuccess && I > 0)
+    e = launch_gemm(qx, wu, u, M, I, H, d_sx, d_su, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
+  if (e == hipSuccess && I > 0)
+    e = launch_silu_mul(g, u, qh, M * I, d_sh, ew_blocks(cus), stream);
+  if (e == hipSuccess)
+    e = launch_gemm(qh, wd, y, M, H, I, d_sh, d_sd, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
+  return hip_status(e);
+}
+
+size_t qkv_fp8_workspace(int64_t M, int64_t H) {
+  if (M < 0 || H < 0) return 0;
+  return round256((size_t)M * H);
+}
+
+int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
+            const uint8_t* wq, int64_t Nq, const float* d_sq,
+            const uint8_t* wk, int64_t Nk, const float* d_sk,
+            const uint8_t* wv, int64_t Nv, const float* d_sv, uint16_t* yq,
+            uint16_t* yk, uint16_t* yv, void* ws, size_t ws_bytes, int accum,
+            hipStream_t stream) {
+  if (!d_sx || !d_sq || !d_sk || !d_sv) return FP8MOT_ERR_UNSUPPORTED;
+  if (accum != FP8MOT_ACC_EXACT && accum != FP8MOT_ACC_FP8_MFMA) return FP8MOT_ERR_INVALID_ARG;
+  if (M < 0 || H < 0 || Nq < 0 || Nk < 0 || Nv < 0 || (H % 16) != 0)
+    return FP8MOT_ERR_INVALID_ARG;
+  if (M > INT32_MAX || H > INT32_MAX || Nq > INT32_MAX || Nk > INT32_MAX || Nv > INT32_MAX)
+    return FP8MOT_ERR_INVALID_ARG;
+  if (M == 0) return FP8MOT_OK;
+  if (!x || !wq || !wk || !wv || !yq || !yk || !yv) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv) ||
+      !aligned16(yq) || !aligned16(yk) || !aligned16(yv))
+    return FP8MOT_ERR_MISALIGNED;
+  if (ws == nullptr || !aligned256(ws) || ws_bytes < qkv_fp8_workspace(M, H))
+    return FP8MOT_ERR_WORKSPACE;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  uint8_t* qx = static_cast<uint8_t*>(ws);
+  hipError_t e = hipSuccess;
+  if (H > 0) {
+    g_quant_launches.fetch_add(1);
+    e = launch_quant_static(x, qx, M * H, d_sx, ew_blocks(cus), stream);
+  }
+  if (e == hipSuccess && Nq > 0)
+    e = launch_gemm(qx, wq, yq, M, Nq, H, d_sx, d_sq, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
+  if (e == hipSuccess && Nk > 0)
+    e = launch_gemm(qx, wk, yk, M, Nk, H, d_sx, d_sk, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
+  if (e == hipSuccess && Nv > 0)
+    e = launch_gemm(qx, wv, yv, M, Nv, H, d_sx, d_sv, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
+  return hip_status(e);
+}
+
+static int observe_common(const uint16_t* x, const uint16_t* u, int64_t n,
+                          void* d_state, int mode, float c, hipStream_t stream) {
+  if (mode != FP8MOT_OBS_MAX && mode != FP8MOT_OBS_MOVING_AVG) return FP8MOT_ERR_INVALID_ARG;
+  if (mode == FP8MOT_OBS_MOVING_AVG && !std::isfinite(c)) return FP8MOT_ERR_INVALID_ARG;
+  if (n < 1 || x == nullptr || d_state == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(d_state) || (u != nullptr && !aligned16(u)))
+    return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_observe(x, u, n, static_cast<fp8mot_observer_state_dev*>(d_state),
+                                   mode, c, ew_blocks(cus), stream));
+}
+
+int fp8_observe(const uint16_t* x, int64_t n, void* d_state, int mode, float c,
+                hipStream_t stream) {
+  return observe_common(x, nullptr, n, d_state, mode, c, stream);
+}
+
+int fp8_observe_swiglu(const uint16_t* g, const uint16_t* u, int64_t n,
+                       void* d_state, int mode, float c, hipStream_t stream) {
+  if (u == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  return observe_common(g, u, n, d_state, mode, c, stream);
+}
+
+int fp8_scale_from_state(const void* d_state, float* d_scale, hipStream_t stream) {
+  if (d_state == nullptr || d_scale == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(d_state)) return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_scale_from_state(
+      static_cast<const fp8mot_observer_state_dev*>(d_state), d_scale, stream));
+}
+
+int fp8_check_shared_scale(const float* h_scales, int n) {
+  if (h_scales == nullptr || n < 1) return FP8MOT_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (!std::isfinite(h_scales[i]) || !(h_scales[i] > 0.0f)) return FP8MOT_ERR_INVALID_ARG;
+  uint32_t b0;
+  std::memcpy(&b0, &h_scales[0], 4);
+  for (int i = 1; i < n; ++i) {
+    uint32_t b;
+    std::memcpy(&b, &h_scales[i], 4);
+    if (b != b0) return FP8MOT_ERR_SCALE_MISMATCH;
+  }
+  return FP8MOT_OK;
+}
+
+}  // extern "C"
+
+static_assert(sizeof(fp8mot_observer_state) == 16, "observer state is 16 bytes");
+static_assert(sizeof(fp8mot_observer_state_dev) == sizeof(fp8mot_observer_state),
+              "device and public observer state agree");

@@ -1,0 +1,83 @@
+// Device helpers shared by the libfp8mot kernels (gfx950 only).
+//
+// Number formats follow the model card "Cosmos3-Nano-Policy-DROID, FP8 + RTN
+// + moving-average activation observer", section "Scheme": FP8 E4M3 weights
+// and activations, one scale per tensor.  The E4M3 variant is OCP E4M3FN
+// (bias 7, no infinities, S.1111.111 = NaN, largest finite 448).  Rounding is
+// to nearest with ties to the even code; overflow saturates to +-448 so that
+// an activation above the calibrated range is clipped; NaN becomes 0x7F and
+// the sign of zero is kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8mot {
+
+// BF16 bit pattern -> FP32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// FP32 -> BF16 bit pattern, round to nearest even; NaN -> quiet NaN 0x7FC0
+// with the sign kept.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// FP32 -> E4M3FN code with integer round-to-nearest-even on the bit pattern.
+//  |v| >= 448 (and Inf): saturate to 0x7E.
+//  [2^-6, 448): keep exponent and 3 mantissa bits, RNE on the 20 dropped
+//    bits; a carry moves into the exponent as it should; re-bias 127 -> 7.
+//  below 2^-6: E4M3 subnormals are multiples of 2^-9; adding 2^14, whose
+//    FP32 ulp is 2^-9, rounds |v| to that grid (RNE) in one addition, and
+//    the integer difference of the bit patterns is the code (0..8, where 8
+//    is the smallest normal, 0x08).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {
+    code = 0x7Eu;
+  } else if (a >= 0x3C800000u) {
+    code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - 0x3C0u;
+  } else {
+    const float f = __fadd_rn(__uint_as_float(a), 16384.0f);
+    code = __float_as_uint(f) - 0x46800000u;
+  }
+  code |= (u >> 24) & 0x80u;
+  return a > 0x7F800000u ? 0x7Fu : code;
+}
+
+// Four FP32 values -> four E4M3 codes packed little-endian in a dword, using
+// the gfx950 conversion instruction.  Clamping to [-448, 448] first makes it
+// saturate; over every non-NaN FP32 input this gives exactly the codes of
+// e4m3_encode (checked by running both over all 2^32 bit patterns).  NaN
+// inputs are patched to 0x7F afterwards.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  const float cc = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  const float cd = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, (int)w, true);
+  if (a != a) w = (w & 0xFFFFFF00u) | 0x0000007Fu;
+  if (b != b) w = (w & 0xFFFF00FFu) | 0x00007F00u;
+  if (c != c) w = (w & 0xFF00FFFFu) | 0x007F0000u;
+  if (d != d) w = (w & 0x00FFFFFFu) | 0x7F000000u;
+  return w;
+}
+
+// SiLU(g) * u in FP32: g * (1 / (1 + exp(-g))) * u, with the hardware
+// exponential and reciprocal (about 1 ulp each).  For very negative g,
+// exp(-g) overflows to +Inf, its reciprocal is 0 and the result is a zero
+// with the sign of g * u, as in exact arithmetic.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __expf(-g);
+  const float s = __fmul_rn(g, __builtin_amdgcn_rcpf(__fadd_rn(1.0f, e)));
+  return __fmul_rn(s, u);
+}
+
+}  // namespace fp8mot

@@ -1,0 +1,42 @@
+// Internal launcher interface between the C ABI (capi.hip) and the kernels.
+// Launchers assume validated arguments: non-negative sizes, 16-byte aligned
+// pointers, K % 16 == 0, non-null scales.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8mot {
+
+// Device layout of fp8mot_observer_state (include/fp8mot.h).
+struct fp8mot_observer_state_dev {
+  float m;
+  int32_t count;
+  uint32_t pending;  // FP32 bit pattern of the running amax of the current call
+  uint32_t reserved;
+};
+
+hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
+                               const float* d_scale, int max_blocks,
+                               hipStream_t stream);
+
+hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
+                           int64_t n, const float* d_s, int max_blocks,
+                           hipStream_t stream);
+
+// u == nullptr: amax of the BF16 tensor x; otherwise amax of silu(x) * u.
+hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,
+                          fp8mot_observer_state_dev* st, int mode, float c,
+                          int max_blocks, hipStream_t stream);
+
+hipError_t launch_scale_from_state(const fp8mot_observer_state_dev* st,
+                                   float* scale, hipStream_t stream);
+
+// FP8 GEMM y[M,N] = (qa[M,K] . qb[N,K]^T) * (sx*sw), out_kind per fp8mot_out,
+// accum per fp8mot_acc (0: F16 MFMA on exactly decoded codes, 1: FP8 MFMA).
+hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
+                       int64_t M, int64_t N, int64_t K, const float* sx,
+                       const float* sw, int out_kind, const float* sy,
+                       int accum, int num_cus, hipStream_t stream);
+
+}  // namespace fp8mot

@@ -1,0 +1,114 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol
+the header declares, and refuses bad arguments before touching a device.
+No kernel is launched here (no GPU in this environment)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8mot.h")
+
+
+def _lib():
+    from mlp_fp8_quant_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libfp8mot.so is not built (run __graft_entry__.build())")
+    return L.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared_functions()
+    for n in ("fp8_quant_static", "fp8_linear", "silu_mul_2in_fp8",
+              "gated_mlp_fp8", "qkv_fp8", "fp8_observe", "fp8_scale_from_state",
+              "fp8_check_shared_scale"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    from mlp_fp8_quant_amd._lib import SIGNATURES
+    assert set(SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings():
+    lib = _lib()
+    for st in range(7):
+        assert lib.fp8mot_status_string(st)
+    assert lib.fp8mot_status_string(99) == b"unknown status"
+
+
+def test_check_shared_scale_host_logic():
+    import mlp_fp8_quant_amd as fp8
+    fp8.fp8_check_shared_scale([0.5, 0.5, 0.5])
+    cases = {3: [0.5, 0.25], 1: [0.5, float("nan")]}
+    for status, sc in cases.items():
+        with pytest.raises(fp8.Fp8motError) as e:
+            fp8.fp8_check_shared_scale(sc)
+        assert e.value.status == status
+    for sc in ([], [0.0, 0.0], [-1.0], [float("inf")]):
+        with pytest.raises(fp8.Fp8motError) as e:
+            fp8.fp8_check_shared_scale(sc)
+        assert e.value.status == 1
+
+
+def test_workspace_sizes():
+    lib = _lib()
+    M, H, I = 2048, 2048, 8192
+    r = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert lib.gated_mlp_fp8_workspace(M, H, I) == r(M * H) + 2 * r(2 * M * I) + r(M * I)
+    assert lib.qkv_fp8_workspace(3072, 4096) == 3072 * 4096
+    assert lib.gated_mlp_fp8_workspace(-1, 1, 1) == 0
+
+
+def test_refusals_before_any_device_access():
+    lib = _lib()
+    P = ctypes.c_void_p
+    fake = P(0x10000)        # never dereferenced: every case below is refused
+    odd = P(0x10001)         # earlier, by argument validation alone
+    null = P(0)
+    s = fake
+    # NULL scale = dynamic quantization -> UNSUPPORTED
+    assert lib.fp8_quant_static(fake, fake, 16, null, null) == 4
+    assert lib.silu_mul_2in_fp8(fake, fake, fake, 16, null, null) == 4
+    assert lib.fp8_linear(fake, fake, fake, 4, 4, 16, null, s, 0, null, 0, null) == 4
+    assert lib.fp8_linear(fake, fake, fake, 4, 4, 16, s, s, 1, null, 0, null) == 4
+    # negative sizes, K % 16, bad enums -> INVALID_ARG
+    assert lib.fp8_quant_static(fake, fake, -1, s, null) == 1
+    assert lib.fp8_linear(fake, fake, fake, 4, 4, 24, s, s, 0, null, 0, null) == 1
+    assert lib.fp8_linear(fake, fake, fake, -4, 4, 16, s, s, 0, null, 0, null) == 1
+    assert lib.fp8_linear(fake, fake, fake, 4, 4, 16, s, s, 7, null, 0, null) == 1
+    assert lib.fp8_observe(fake, 16, fake, 5, ctypes.c_float(0.01), null) == 1
+    assert lib.fp8_observe(fake, 0, fake, 0, ctypes.c_float(0.01), null) == 1
+    assert lib.fp8_observe(fake, 16, fake, 1, ctypes.c_float(float("nan")), null) == 1
+    # NULL data pointers with a non-empty size -> INVALID_ARG
+    assert lib.fp8_quant_static(null, fake, 16, s, null) == 1
+    # empty tensors are a valid no-op
+    assert lib.fp8_quant_static(null, null, 0, s, null) == 0
+    assert lib.fp8_linear(null, null, null, 0, 4, 16, s, s, 0, null, 0, null) == 0
+    # misaligned base pointers -> MISALIGNED
+    assert lib.fp8_quant_static(odd, fake, 16, s, null) == 2
+    assert lib.silu_mul_2in_fp8(fake, odd, fake, 16, s, null) == 2
+    assert lib.fp8_linear(fake, fake, odd, 4, 4, 16, s, s, 0, null, 0, null) == 2
+    # composites: workspace too small -> WORKSPACE
+    assert lib.qkv_fp8(fake, 4, 16, s, fake, 4, s, fake, 4, s, fake, 4, s,
+                       fake, fake, fake, fake, 8, 0, null) == 6
+    assert lib.gated_mlp_fp8(fake, 4, 16, 32, s, fake, s, fake, s, s, fake, s,
+                             fake, null, 0, 0, null) == 6
+    assert lib.gated_mlp_fp8(fake, 4, 16, 32, null, fake, s, fake, s, s, fake, s,
+                             fake, fake, 1 << 20, 0, null) == 4
+    # unknown accumulation engine -> INVALID_ARG
+    assert lib.fp8_linear(fake, fake, fake, 4, 4, 16, s, s, 0, null, 2, null) == 1
+    assert lib.gated_mlp_fp8(fake, 4, 16, 32, s, fake, s, fake, s, s, fake, s,
+                             fake, fake, 1 << 20, 5, null) == 1

@@ -1,0 +1,233 @@
+"""GPU parity: the FP8 GEMM (fp8_linear) against the oracle's exact sum.
+
+The default engine (ACC_EXACT) must meet the stated tolerance on every
+output.  The native FP8 MFMA engine (ACC_FP8_MFMA) is held to the bound
+derived from the gfx950 FP8 MFMA's group accumulation; how many of its
+outputs exceed 1e-5 * sum|terms| is reported."""
+
+import numpy as np
+import pytest
+import torch
+
+import mlp_fp8_quant_amd as fp8
+from mlp_fp8_quant_amd import workloads
+from oracle import linear as olin
+from oracle.formats import (E4M3_TABLE, bf16_ulps, e4m3_decode, e4m3_encode,
+                            f32_to_bf16)
+
+from gpu_util import (check_fp8_tolerance, check_gemm_bf16, check_gemm_f32,
+                      check_gemm_fp8_engine, device, fp8_mfma_group_bound,
+                      host_bits, host_f32, host_u8, scalar, to_dev_u8)
+
+pytestmark = pytest.mark.gpu
+
+ENGINES = [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA]
+
+
+def _codes(rng, shape):
+    c = rng.integers(0, 256, shape, dtype=np.int64).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E
+    return c
+
+
+def _run(qa, qb, sx, sw, dev, kinds=(fp8.OUT_F32, fp8.OUT_BF16), sy=None,
+         accum=fp8.ACC_EXACT):
+    da, db = to_dev_u8(qa, dev), to_dev_u8(qb, dev)
+    dsx, dsw = scalar(sx, dev), scalar(sw, dev)
+    dsy = scalar(sy, dev) if sy is not None else None
+    return {k: fp8.fp8_linear(da, db, dsx, dsw, k, dsy, accum=accum) for k in kinds}
+
+
+@pytest.mark.parametrize("accum", ENGINES)
+def test_all_code_pairs_single_term(accum):
+    # every non-NaN code pair as a K = 16 dot product with only k = 0 set:
+    # the FP32 output must be exactly dec(a)*dec(b) (this pins the decoding of
+    # every code, subnormals included) and the BF16 output its exact value;
+    # an exact zero may come out as either signed zero
+    dev = device()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    qa = np.zeros((254, 16), np.uint8)
+    qb = np.zeros((254, 16), np.uint8)
+    qa[:, 0] = codes
+    qb[:, 0] = codes
+    out = _run(qa, qb, 1.0, 1.0, dev, accum=accum)
+    v = E4M3_TABLE[codes]
+    prod = np.outer(v, v)
+    assert np.array_equal(host_f32(out[fp8.OUT_F32]).astype(np.float64), prod)
+    assert bf16_ulps(host_bits(out[fp8.OUT_BF16]),
+                     f32_to_bf16(prod.astype(np.float32))).max() == 0
+
+
+@pytest.mark.parametrize("accum", ENGINES)
+def test_identity_weight_returns_decoded_input(accum):
+    dev = device()
+    rng = np.random.default_rng(30)
+    qx = _codes(rng, (300, 256))
+    eye = np.zeros((256, 256), np.uint8)
+    eye[np.arange(256), np.arange(256)] = 0x38
+    out = _run(qx, eye, 1.0, 1.0, dev, kinds=(fp8.OUT_F32,), accum=accum)
+    assert np.array_equal(host_f32(out[fp8.OUT_F32]).astype(np.float64),
+                          e4m3_decode(qx))
+
+
+SHAPES = [(1, 1, 16), (3, 5, 32), (17, 13, 48), (64, 64, 64), (128, 128, 128),
+          (129, 127, 144), (300, 200, 4096), (257, 385, 1040), (16, 17, 0)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_random_codes_ragged_exact(M, N, K):
+    dev = device()
+    rng = np.random.default_rng(M * 1000 + N + K)
+    qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx, sw = np.float32(0.0213), np.float32(1.7e-4)
+    out = _run(qa, qb, sx, sw, dev)
+    S, A = olin.gemm_exact(qa, qb)
+    alpha = olin.epilogue_alpha(sx, sw)
+    y32 = host_f32(out[fp8.OUT_F32])
+    check_gemm_f32(y32, S, A, alpha)
+    yb = host_bits(out[fp8.OUT_BF16])
+    assert np.array_equal(yb, f32_to_bf16(y32))  # same kernel, same sums
+    check_gemm_bf16(yb, y32, S, A, alpha)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_random_codes_ragged_fp8_engine(M, N, K):
+    dev = device()
+    rng = np.random.default_rng(M * 1000 + N + K)
+    qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx, sw = np.float32(0.0213), np.float32(1.7e-4)
+    out = _run(qa, qb, sx, sw, dev, accum=fp8.ACC_FP8_MFMA)
+    S, A = olin.gemm_exact(qa, qb)
+    alpha = olin.epilogue_alpha(sx, sw)
+    y32 = host_f32(out[fp8.OUT_F32])
+    check_gemm_fp8_engine(y32, S, A, alpha, fp8_mfma_group_bound(qa, qb))
+    assert np.array_equal(host_bits(out[fp8.OUT_BF16]), f32_to_bf16(y32))
+
+
+@pytest.mark.parametrize("accum", ENGINES)
+def test_fp8_output_epilogue(accum):
+    dev = device()
+    rng = np.random.default_rng(31)
+    x = workloads.activations(rng, 256, 512)
+    w = workloads.weights(rng, 384, 512, 0.02)
+    sx = olin.scale_from_amax(olin.amax_f32(x))
+    qa = olin.quant_static(x, sx)
+    qb, sw = olin.rtn_weight(w)
+    S, _ = olin.gemm_exact(qa, qb)
+    sy = np.float32(np.max(np.abs(S)) * olin.epilogue_alpha(sx, sw) / 448)
+    out = _run(qa, qb, sx, sw, dev, kinds=(fp8.OUT_FP8,), sy=sy, accum=accum)
+    got = host_u8(out[fp8.OUT_FP8])
+    if accum == fp8.ACC_EXACT:
+        check_fp8_tolerance(got, olin.epilogue_fp8(S, sx, sw, sy))
+        return
+    # native FP8 MFMA engine: the code must lie within one step of the codes
+    # of the two ends of the accumulation's error interval
+    alpha = np.float64(olin.epilogue_alpha(sx, sw))
+    b = alpha * (fp8_mfma_group_bound(qa, qb) + 1e-5 * olin.gemm_exact(qa, qb)[1])
+    y = alpha * S
+    lo = e4m3_encode(((y - b) / np.float64(sy)).astype(np.float32))
+    hi = e4m3_encode(((y + b) / np.float64(sy)).astype(np.float32))
+    o = lambda c: np.where(c & 0x80, -(c.astype(np.int64) & 0x7F), c.astype(np.int64) & 0x7F)  # noqa: E731
+    assert np.all((o(got) >= o(lo) - 1) & (o(got) <= o(hi) + 1))
+
+
+def _linear_case(x_bits, w_bits, dev, rows=None, accum=fp8.ACC_EXACT):
+    """Quantize x and w as the method does and compare one projection."""
+    sx = olin.scale_from_amax(olin.amax_f32(x_bits))
+    qx = olin.quant_static(x_bits, sx)
+    qw, sw = olin.rtn_weight(w_bits)
+    out = _run(qx, qw, sx, sw, dev, accum=accum)
+    y32 = host_f32(out[fp8.OUT_F32])
+    yb = host_bits(out[fp8.OUT_BF16])
+    if rows is not None:
+        qx, y32, yb = qx[rows], y32[rows], yb[rows]
+    S, A = olin.gemm_exact(qx, qw)
+    alpha = olin.epilogue_alpha(sx, sw)
+    if accum == fp8.ACC_EXACT:
+        check_gemm_f32(y32, S, A, alpha)
+        return check_gemm_bf16(yb, y32, S, A, alpha)
+    sub = slice(0, 16)  # the group bound is costly; evaluate it on 16 rows
+    frac = check_gemm_fp8_engine(y32[sub], S[sub], A[sub], alpha,
+                                 fp8_mfma_group_bound(qx[sub], qw))
+    print(f"fp8 engine: {frac:.4%} of sampled outputs beyond 1e-5 sum|terms|")
+    return frac
+
+
+@pytest.mark.parametrize("accum", ENGINES)
+def test_single_linear_config(accum):
+    dev = device()
+    wl = workloads.single_linear()
+    _linear_case(wl.x, wl.weights["w"], dev, accum=accum)
+
+
+@pytest.mark.parametrize("accum", ENGINES)
+def test_gen_mlp_gate_up_down_shapes(accum):
+    dev = device()
+    wl = workloads.gen_tower_mlp()
+    for name in ("gate", "up"):
+        _linear_case(wl.x, wl.weights[name], dev, accum=accum)
+    # down: its input is the [2048, 8192] SwiGLU output; a draw of the same
+    # shape stands in here (the chained case is in the composite tests)
+    h = workloads.activations(np.random.default_rng(5), 2048, 8192)
+    _linear_case(h, wl.weights["down"], dev, accum=accum)
+
+
+def test_split_qkv_shapes():
+    dev = device()
+    wl = workloads.split_qkv()
+    for name in ("q", "k", "v"):
+        _linear_case(wl.x, wl.weights[name], dev)
+
+
+def test_two_tower_shapes_sampled_rows():
+    dev = device()
+    ws = workloads.layer_weights("gen")
+    rows = np.sort(np.random.default_rng(3).choice(4096, 256, replace=False))
+    for p in ("q", "gate", "down"):
+        site = {"q": "qkv", "gate": "gateup", "down": "down"}[p]
+        x = workloads.forward_input("gen", site)
+        _linear_case(x, ws[p], dev, rows=rows)
+    ws = workloads.layer_weights("und")
+    for p in ("q", "up", "down"):
+        site = {"q": "qkv", "up": "gateup", "down": "down"}[p]
+        _linear_case(workloads.forward_input("und", site), ws[p], dev)
+
+
+def test_super_mlp_shapes_sampled_rows():
+    dev = device()
+    rng = np.random.default_rng(0)
+    x = workloads.activations(rng, 16384, 5120)
+    w = workloads.weights(rng, 25600, 5120, 0.015)
+    rows = np.sort(np.random.default_rng(4).choice(16384, 64, replace=False))
+    _linear_case(x, w, dev, rows=rows)
+
+
+@pytest.mark.parametrize("accum", ENGINES)
+def test_deterministic(accum):
+    dev = device()
+    rng = np.random.default_rng(32)
+    qa, qb = _codes(rng, (512, 1024)), _codes(rng, (768, 1024))
+    a = _run(qa, qb, 0.1, 0.2, dev, kinds=(fp8.OUT_F32,), accum=accum)[fp8.OUT_F32]
+    b = _run(qa, qb, 0.1, 0.2, dev, kinds=(fp8.OUT_F32,), accum=accum)[fp8.OUT_F32]
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_refusals():
+    dev = device()
+    qa = torch.zeros((4, 24), dtype=torch.uint8, device=dev)
+    qb = torch.zeros((4, 24), dtype=torch.uint8, device=dev)
+    s = scalar(1.0, dev)
+    with pytest.raises(fp8.Fp8motError) as e:   # K % 16 != 0
+        fp8.fp8_linear(qa, qb, s, s)
+    assert e.value.status == 1
+    qa = torch.zeros((4, 32), dtype=torch.uint8, device=dev)
+    qb = torch.zeros((4, 32), dtype=torch.uint8, device=dev)
+    with pytest.raises(fp8.Fp8motError) as e:   # dynamic quantization
+        fp8.fp8_linear(qa, qb, None, s)
+    assert e.value.status == 4
+    with pytest.raises(fp8.Fp8motError) as e:   # FP8 out needs its scale
+        fp8.fp8_linear(qa, qb, s, s, fp8.OUT_FP8, None)
+    assert e.value.status == 4
+    with pytest.raises(fp8.Fp8motError) as e:   # unknown engine
+        fp8.fp8_linear(qa, qb, s, s, accum=7)
+    assert e.value.status == 1

@@ -1,0 +1,207 @@
+"""GPU parity: static quantization, RTN weights and the observers, bit-exact
+against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import mlp_fp8_quant_amd as fp8
+from mlp_fp8_quant_amd import workloads
+from oracle import linear as olin
+from oracle import observer as oobs
+
+from gpu_util import device, host_f32, host_u8, scalar, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+ALL_BF16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -7, 2.0 ** 5, 0.0123, 20.0 / 448,
+                                   3.7e-3, 1.337, 1e-30, 7.5e30])
+def test_quant_exhaustive_bf16(scale):
+    dev = device()
+    s = np.float32(scale)
+    q = fp8.fp8_quant_static(to_dev_bf16(ALL_BF16, dev), scalar(s, dev))
+    assert np.array_equal(host_u8(q), olin.quant_static(ALL_BF16, s))
+
+
+def test_quant_exhaustive_random_scales():
+    dev = device()
+    x = to_dev_bf16(ALL_BF16, dev)
+    rng = np.random.default_rng(20)
+    for s in np.exp(rng.uniform(-12, 8, 16)).astype(np.float32):
+        q = fp8.fp8_quant_static(x, scalar(s, dev))
+        assert np.array_equal(host_u8(q), olin.quant_static(ALL_BF16, s)), s
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 15, 16, 17, 255, 4097, 1_000_003])
+def test_quant_ragged_lengths(n):
+    dev = device()
+    rng = np.random.default_rng(n)
+    bits = rng.integers(0, 65536, n, dtype=np.int64).astype(np.uint16)
+    s = np.float32(0.031)
+    q = fp8.fp8_quant_static(to_dev_bf16(bits, dev), scalar(s, dev))
+    assert np.array_equal(host_u8(q), olin.quant_static(bits, s))
+
+
+@pytest.mark.parametrize("name", ["single_linear", "gen_mlp", "split_qkv"])
+def test_quant_config_activations(name):
+    dev = device()
+    wl = workloads.CONFIGS[name]()
+    s = olin.scale_from_amax(olin.amax_f32(wl.x))
+    q = fp8.fp8_quant_static(to_dev_bf16(wl.x, dev), scalar(s, dev))
+    assert np.array_equal(host_u8(q), olin.quant_static(wl.x, s))
+
+
+def test_quant_super_mlp_activation_sampled():
+    # 16384 x 5120: every code checked on a seeded sample of 4M positions
+    dev = device()
+    rng = np.random.default_rng(0)
+    x = workloads.activations(rng, 16384, 5120, outliers=True)
+    s = olin.scale_from_amax(olin.amax_f32(x))
+    q = host_u8(fp8.fp8_quant_static(to_dev_bf16(x, dev), scalar(s, dev))).ravel()
+    pos = np.random.default_rng(1).choice(x.size, 4_000_000, replace=False)
+    assert np.array_equal(q[pos], olin.quant_static(x.ravel()[pos], s))
+
+
+@pytest.mark.parametrize("name", ["single_linear", "gen_mlp"])
+def test_rtn_weights_on_gpu_match_oracle(name):
+    dev = device()
+    wl = workloads.CONFIGS[name]()
+    for w in wl.weights.values():
+        q, s = fp8.rtn_weight(to_dev_bf16(w, dev))
+        oq, os_ = olin.rtn_weight(w)
+        assert host_f32(s)[0].view(np.uint32) == np.float32(os_).view(np.uint32)
+        assert np.array_equal(host_u8(q), oq)
+
+
+def _state_host(st):
+    a = st.cpu().numpy()
+    return a[:1].view(np.float32)[0], int(a[1]), int(a[2])
+
+
+def test_observer_amax_and_max_exact():
+    dev = device()
+    rng = np.random.default_rng(21)
+    st = fp8.new_observer_state(dev)
+    ost = oobs.ObserverState()
+    for t in range(20):
+        n = int(rng.integers(1, 300_000))
+        bits = workloads.to_bf16_bits(rng.standard_normal(n).astype(np.float32)
+                                      * np.float32(rng.uniform(0.1, 50)))
+        fp8.fp8_observe(to_dev_bf16(bits, dev), st, fp8.OBS_MAX)
+        oobs.observe(ost, oobs.call_amax(bits), oobs.OBS_MAX)
+        m, count, pending = _state_host(st)
+        assert m.view(np.uint32) == np.float32(ost.m).view(np.uint32)
+        assert count == t + 1 and pending == 0
+    s = fp8.fp8_scale_from_state(st)
+    assert host_f32(s)[0] == olin.scale_from_amax(ost.m)
+
+
+def test_observer_nan_propagates():
+    dev = device()
+    bits = workloads.to_bf16_bits(np.ones(1000, np.float32))
+    st = fp8.new_observer_state(dev)
+    fp8.fp8_observe(to_dev_bf16(bits, dev), st, fp8.OBS_MAX)
+    bits[123] = 0x7FC1
+    fp8.fp8_observe(to_dev_bf16(bits, dev), st, fp8.OBS_MAX)
+    assert np.isnan(_state_host(st)[0])
+
+
+@pytest.mark.parametrize("mode", [fp8.OBS_MAX, fp8.OBS_MOVING_AVG])
+def test_two_tower_calibration_und_full(mode):
+    # 256 calibration calls of the und tower at full size ([512, 4096] group
+    # inputs, [512, 12288] down input), both observers, bit-exact
+    dev = device()
+    for site in workloads.SITES:
+        base = workloads.calib_base("und", site)
+        dbase = to_dev_bf16(base, dev).view(-1)
+        st = fp8.new_observer_state(dev)
+        ost = oobs.ObserverState()
+        for t in range(workloads.CALIB_CALLS):
+            pos, gain = workloads.calib_spikes("und", site, t, base.size)
+            x = workloads.calib_call(base, pos, gain)
+            dx = dbase.clone()
+            dpos = torch.from_numpy(pos).to(dev)
+            dx[dpos] = to_dev_bf16(x.ravel()[pos], dev)
+            fp8.fp8_observe(dx, st, mode, 0.01)
+            oobs.observe(ost, oobs.call_amax(x), mode, 0.01)
+        m, count, _ = _state_host(st)
+        assert count == 256
+        assert m.view(np.uint32) == np.float32(ost.m).view(np.uint32), site
+
+
+def test_two_tower_gen_calls_sampled():
+    # gen tower, [4096, 12288] down input: a few calls at full size
+    dev = device()
+    base = workloads.calib_base("gen", "down")
+    dbase = to_dev_bf16(base, dev).view(-1)
+    for mode in (fp8.OBS_MAX, fp8.OBS_MOVING_AVG):
+        st = fp8.new_observer_state(dev)
+        ost = oobs.ObserverState()
+        for t in range(4):
+            pos, gain = workloads.calib_spikes("gen", "down", t, base.size)
+            x = workloads.calib_call(base, pos, gain)
+            dx = dbase.clone()
+            dx[torch.from_numpy(pos).to(dev)] = to_dev_bf16(x.ravel()[pos], dev)
+            fp8.fp8_observe(dx, st, mode, 0.01)
+            oobs.observe(ost, oobs.call_amax(x), mode, 0.01)
+        m = _state_host(st)[0]
+        assert m.view(np.uint32) == np.float32(ost.m).view(np.uint32)
+
+
+def test_moving_average_scales_saturate_forward_inputs():
+    # the moving-average scale sits below the per-call maxima of the spiky
+    # calls, so quantizing the spikiest call under it must clip; the forward
+    # draw is quantized bit-exactly as well
+    dev = device()
+    base = workloads.calib_base("und", "qkv")
+    dbase = to_dev_bf16(base, dev).view(-1)
+    st = fp8.new_observer_state(dev)
+    best, best_amax = None, -1.0
+    for t in range(workloads.CALIB_CALLS):
+        pos, gain = workloads.calib_spikes("und", "qkv", t, base.size)
+        dx = dbase.clone()
+        x = workloads.calib_call(base, pos, gain)
+        dx[torch.from_numpy(pos).to(dev)] = to_dev_bf16(x.ravel()[pos], dev)
+        fp8.fp8_observe(dx, st, fp8.OBS_MOVING_AVG, 0.01)
+        a = float(oobs.call_amax(x))
+        if a > best_amax:
+            best, best_amax = x, a
+    s = fp8.fp8_scale_from_state(st)
+    q = host_u8(fp8.fp8_quant_static(to_dev_bf16(best, dev), s))
+    assert np.count_nonzero((q & 0x7F) == 0x7E) > 0
+    assert np.array_equal(q, olin.quant_static(best, host_f32(s)[0]))
+    fwd = workloads.forward_input("und", "qkv")
+    qf = host_u8(fp8.fp8_quant_static(to_dev_bf16(fwd, dev), s))
+    assert np.array_equal(qf, olin.quant_static(fwd, host_f32(s)[0]))
+
+
+def test_observe_swiglu_amax():
+    dev = device()
+    rng = np.random.default_rng(22)
+    g = workloads.to_bf16_bits(rng.standard_normal(100_003).astype(np.float32) * 3)
+    u = workloads.to_bf16_bits(rng.standard_normal(100_003).astype(np.float32) * 2)
+    st = fp8.new_observer_state(dev)
+    fp8.fp8_observe_swiglu(to_dev_bf16(g, dev), to_dev_bf16(u, dev), st, fp8.OBS_MAX)
+    m = _state_host(st)[0]
+    from oracle.swiglu import silu_mul_f64
+    ref = np.max(np.abs(silu_mul_f64(g, u)))
+    # FP32 evaluation with hardware exp/rcp: a few FP32 ulps
+    assert abs(float(m) - ref) <= 8 * 2.0 ** -23 * ref
+
+
+def test_refusals():
+    dev = device()
+    x = to_dev_bf16(ALL_BF16[:64], dev)
+    with pytest.raises(fp8.Fp8motError) as e:
+        fp8.fp8_quant_static(x, None)
+    assert e.value.status == 4
+    with pytest.raises(ValueError):
+        fp8.fp8_quant_static(x.view(8, 8).t(), scalar(1.0, dev))
+    # misaligned base pointer: refused, not handled on a slow path
+    xb = to_dev_bf16(ALL_BF16[:80], dev)[1:65]
+    with pytest.raises(fp8.Fp8motError) as e:
+        fp8.fp8_quant_static(xb, scalar(1.0, dev))
+    assert e.value.status == 2

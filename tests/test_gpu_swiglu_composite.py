@@ -1,0 +1,235 @@
+"""GPU parity: two-input SwiGLU with FP8 output, and the composites
+gated_mlp_fp8 / qkv_fp8 (bitwise equal to their parts, one quantization)."""
+
+import numpy as np
+import pytest
+import torch
+
+import mlp_fp8_quant_amd as fp8
+from mlp_fp8_quant_amd import workloads
+from oracle import linear as olin
+from oracle.formats import e4m3_decode
+from oracle.swiglu import silu_mul_f64, silu_mul_fp8
+
+from gpu_util import (check_fp8_tolerance, check_gemm_bf16, check_gemm_f32,
+                      device, host_bits,
+                      host_u8, scalar, to_dev_bf16, to_dev_u8)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gu(rng, n, sg=3.0, su=2.0):
+    g = workloads.to_bf16_bits(rng.standard_normal(n).astype(np.float32) * np.float32(sg))
+    u = workloads.to_bf16_bits(rng.standard_normal(n).astype(np.float32) * np.float32(su))
+    return g, u
+
+
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 1000, 65537, 2048 * 8192])
+def test_swiglu_random(n):
+    dev = device()
+    rng = np.random.default_rng(n)
+    g, u = _gu(rng, n)
+    s = np.float32(np.max(np.abs(silu_mul_f64(g, u))) / 448)
+    q = fp8.silu_mul_2in_fp8(to_dev_bf16(g, dev), to_dev_bf16(u, dev), scalar(s, dev))
+    check_fp8_tolerance(host_u8(q), silu_mul_fp8(g, u, s))
+
+
+def test_swiglu_rank3_and_saturation():
+    dev = device()
+    rng = np.random.default_rng(40)
+    g, u = _gu(rng, 4 * 96 * 128, 6.0, 4.0)
+    s = np.float32(0.01)  # forces saturation of the large products
+    dg = to_dev_bf16(g, dev).view(4, 96, 128)
+    du = to_dev_bf16(u, dev).view(4, 96, 128)
+    q = fp8.silu_mul_2in_fp8(dg, du, scalar(s, dev))
+    assert q.shape == (4, 96, 128)
+    want = silu_mul_fp8(g, u, s)
+    assert np.count_nonzero((want & 0x7F) == 0x7E) > 0
+    check_fp8_tolerance(host_u8(q).ravel(), want)
+
+
+def test_swiglu_special_values():
+    dev = device()
+    gv = np.array([0.0, -0.0, 0.0, 40.0, 100.0, -1e4, -3e38, 3e38, 17.0, -17.0,
+                   np.inf, -np.inf, np.nan, 1.0, -1.0, 0.5], np.float32)
+    uv = np.array([2.0, 2.0, -2.0, 0.25, -0.125, 1.0, -1.0, 1.0, 3.0, 3.0,
+                   1.0, 1.0, 1.0, 0.0, -0.0, 1e-30], np.float32)
+    g, u = workloads.to_bf16_bits(gv), workloads.to_bf16_bits(uv)
+    s = np.float32(0.05)
+    q = host_u8(fp8.silu_mul_2in_fp8(to_dev_bf16(g, dev), to_dev_bf16(u, dev),
+                                     scalar(s, dev)))
+    assert np.array_equal(q, silu_mul_fp8(g, u, s))
+
+
+def test_swiglu_refuses_strided():
+    dev = device()
+    g = torch.zeros((64, 64), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(ValueError):
+        fp8.silu_mul_2in_fp8(g.t(), g, scalar(1.0, dev))
+
+
+def _mlp_setup(wl, dev):
+    """Scales and device weights of a gated-MLP workload (oracle-side RTN,
+    oracle-side s_h = amax(silu(G) U) / 448 from the oracle's G and U)."""
+    x = wl.x
+    sx = olin.scale_from_amax(olin.amax_f32(x))
+    qx = olin.quant_static(x, sx)
+    q = {}
+    s = {}
+    for k, w in wl.weights.items():
+        q[k], s[k] = olin.rtn_weight(w)
+    Sg, Ag = olin.gemm_exact(qx, q["gate"])
+    Su, Au = olin.gemm_exact(qx, q["up"])
+    G = olin.epilogue_bf16(Sg, sx, s["gate"])
+    U = olin.epilogue_bf16(Su, sx, s["up"])
+    # the down projection's static input scale: amax of the oracle's
+    # silu(G)*U over / 448, fixed once and given to both sides
+    sh = olin.scale_from_amax(np.float32(np.max(np.abs(silu_mul_f64(G, U)))))
+    d = {k: to_dev_u8(v, dev) for k, v in q.items()}
+    sc = {k: scalar(v, dev) for k, v in s.items()}
+    return dict(x=x, sx=sx, qx=qx, q=q, s=s, G=G, U=U, sh=sh, d=d, sc=sc,
+                Sg=Sg, Ag=Ag, Su=Su, Au=Au)
+
+
+def test_gated_mlp_composite_equals_parts_and_oracle():
+    dev = device()
+    wl = workloads.gen_tower_mlp()
+    c = _mlp_setup(wl, dev)
+    dx = to_dev_bf16(c["x"], dev)
+    dsx, dsh = scalar(c["sx"], dev), scalar(c["sh"], dev)
+    before = fp8.debug_quant_launches()
+    y = fp8.gated_mlp_fp8(dx, dsx, c["d"]["gate"], c["sc"]["gate"], c["d"]["up"],
+                          c["sc"]["up"], dsh, c["d"]["down"], c["sc"]["down"])
+    torch.cuda.synchronize()
+    assert fp8.debug_quant_launches() - before == 1   # one shared quantization
+    # the five separate calls
+    qx = fp8.fp8_quant_static(dx, dsx)
+    G = fp8.fp8_linear(qx, c["d"]["gate"], dsx, c["sc"]["gate"])
+    U = fp8.fp8_linear(qx, c["d"]["up"], dsx, c["sc"]["up"])
+    qh = fp8.silu_mul_2in_fp8(G, U, dsh)
+    y2 = fp8.fp8_linear(qh, c["d"]["down"], dsh, c["sc"]["down"])
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    # stage-wise against the oracle
+    assert np.array_equal(host_u8(qx), c["qx"])
+    Gb = host_bits(G)
+    nG = int(np.count_nonzero(Gb != c["G"]))
+    assert nG <= 1e-3 * Gb.size
+    check_fp8_tolerance(host_u8(qh).ravel(),
+                        silu_mul_fp8(c["G"], c["U"], c["sh"]))
+    # end to end: the oracle chain, with the tolerance widened by exactly the
+    # effect of the SwiGLU codes that differ by one step
+    qh_o = silu_mul_fp8(c["G"], c["U"], c["sh"]).reshape(2048, 8192)
+    qh_g = host_u8(qh).reshape(2048, 8192)
+    S, A = olin.gemm_exact(qh_o, c["q"]["down"])
+    alpha = olin.epilogue_alpha(c["sh"], c["s"]["down"])
+    dH = np.abs(e4m3_decode(qh_g) - e4m3_decode(qh_o))
+    extra = dH @ np.abs(e4m3_decode(c["q"]["down"])).T
+    yv = host_bits(y).astype(np.uint32)
+    yf = (yv << 16).view(np.float32).astype(np.float64)
+    ref = np.float64(alpha) * S
+    ulp = np.abs(ref) * 2.0 ** -7 + 1e-300
+    bound = np.float64(alpha) * (extra + 1e-5 * A) + ulp
+    assert np.all(np.abs(yf - ref) <= bound)
+
+
+def test_qkv_composite_equals_parts_and_oracle():
+    dev = device()
+    wl = workloads.split_qkv()
+    sx = olin.scale_from_amax(olin.amax_f32(wl.x))
+    qx = olin.quant_static(wl.x, sx)
+    dx, dsx = to_dev_bf16(wl.x, dev), scalar(sx, dev)
+    qs, ss = {}, {}
+    for k in ("q", "k", "v"):
+        qs[k], ss[k] = olin.rtn_weight(wl.weights[k])
+    assert len({float(v) for v in ss.values()}) == 3  # distinct weight scales
+    d = {k: to_dev_u8(v, dev) for k, v in qs.items()}
+    sc = {k: scalar(v, dev) for k, v in ss.items()}
+    before = fp8.debug_quant_launches()
+    yq, yk, yv = fp8.qkv_fp8(dx, dsx, d["q"], sc["q"], d["k"], sc["k"], d["v"], sc["v"])
+    assert fp8.debug_quant_launches() - before == 1
+    for t in (yq, yk, yv):
+        assert t.is_contiguous() and t.shape == (3072, 4096)
+    dqx = fp8.fp8_quant_static(dx, dsx)
+    assert np.array_equal(host_u8(dqx), qx)
+    for k, y in zip(("q", "k", "v"), (yq, yk, yv)):
+        y2 = fp8.fp8_linear(dqx, d[k], dsx, sc[k])
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+        S, A = olin.gemm_exact(qx, qs[k])
+        y32 = fp8.fp8_linear(dqx, d[k], dsx, sc[k], fp8.OUT_F32)
+        check_gemm_bf16(host_bits(y), y32.cpu().numpy(), S, A,
+                        olin.epilogue_alpha(sx, ss[k]))
+
+
+def test_split_path_keeps_each_members_codes_not_requantized():
+    # Pull request "Description": a fused group re-quantizes each member onto
+    # max(s); the split path keeps s_i * qW_i.  With clearly different weight
+    # scales (checked first, or the test could not tell the two apart) the
+    # GPU output must follow the original codes and differ from the
+    # re-quantized ones.
+    dev = device()
+    rng = np.random.default_rng(42)
+    x = workloads.activations(rng, 128, 512)
+    ws = [workloads.weights(rng, 256, 512, sd) for sd in (0.02, 0.006, 0.045)]
+    sx = olin.scale_from_amax(olin.amax_f32(x))
+    qx = olin.quant_static(x, sx)
+    qs, ss = zip(*[olin.rtn_weight(w) for w in ws])
+    assert len({float(v) for v in ss}) == 3
+    rq, smax = olin.requantize_onto_max(qs, ss)
+    dqx, dsx = to_dev_u8(qx, dev), scalar(sx, dev)
+    for q, sw, r in zip(qs, ss, rq):
+        y = fp8.fp8_linear(dqx, to_dev_u8(q, dev), dsx, scalar(sw, dev), fp8.OUT_F32)
+        y32 = y.cpu().numpy()
+        S, A = olin.gemm_exact(qx, q)
+        check_gemm_f32(y32, S, A, olin.epilogue_alpha(sx, sw))
+        if sw != smax:
+            assert np.count_nonzero(r != q) > 0
+            Sr, _ = olin.gemm_exact(qx, r)
+            y_req = np.float64(olin.epilogue_alpha(sx, smax)) * Sr
+            assert np.count_nonzero(np.abs(y32 - y_req) > 1e-5 * np.float64(
+                olin.epilogue_alpha(sx, sw)) * A) > 0
+
+
+def test_composite_refusals():
+    dev = device()
+    x = torch.zeros((16, 64), dtype=torch.bfloat16, device=dev)
+    w = torch.zeros((64, 64), dtype=torch.uint8, device=dev)
+    s = scalar(1.0, dev)
+    with pytest.raises(fp8.Fp8motError) as e:
+        fp8.qkv_fp8(x, None, w, s, w, s, w, s)
+    assert e.value.status == 4
+    small = torch.empty(16, dtype=torch.uint8, device=dev)
+    with pytest.raises(fp8.Fp8motError) as e:
+        fp8.qkv_fp8(x, s, w, s, w, s, w, s, workspace=small)
+    assert e.value.status == 6
+
+
+@pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+def test_composites_equal_parts_each_engine(accum):
+    # rank-3 input [2, 96, 512]: the composites flatten it to M = 192 rows
+    dev = device()
+    rng = np.random.default_rng(41)
+    x = workloads.activations(rng, 192, 512)
+    ws = {k: workloads.weights(rng, *shp, 0.02)
+          for k, shp in (("g", (1024, 512)), ("u", (1024, 512)), ("d", (512, 1024)))}
+    sx = olin.scale_from_amax(olin.amax_f32(x))
+    q, s = {}, {}
+    for k, w in ws.items():
+        q[k], s[k] = olin.rtn_weight(w)
+    d = {k: to_dev_u8(v, dev) for k, v in q.items()}
+    sc = {k: scalar(v, dev) for k, v in s.items()}
+    dx = to_dev_bf16(x, dev).view(2, 96, 512)
+    dsx, dsh = scalar(sx, dev), scalar(0.05, dev)
+    y = fp8.gated_mlp_fp8(dx, dsx, d["g"], sc["g"], d["u"], sc["u"], dsh, d["d"],
+                          sc["d"], accum=accum)
+    assert y.shape == (2, 96, 512)
+    qx = fp8.fp8_quant_static(dx, dsx)
+    G = fp8.fp8_linear(qx, d["g"], dsx, sc["g"], accum=accum)
+    U = fp8.fp8_linear(qx, d["u"], dsx, sc["u"], accum=accum)
+    y2 = fp8.fp8_linear(fp8.silu_mul_2in_fp8(G, U, dsh), d["d"], dsh, sc["d"],
+                        accum=accum)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    yq, yk, yv = fp8.qkv_fp8(dx, dsx, d["g"], sc["g"], d["u"], sc["u"], d["g"],
+                             sc["g"], accum=accum)
+    assert torch.equal(yq.view(torch.int16), G.view(torch.int16))
+    assert torch.equal(yk.view(torch.int16), U.view(torch.int16))
+    assert torch.equal(yv.view(torch.int16), G.view(torch.int16))
