@@ -34,8 +34,11 @@
 //    double buffered: the global loads of stage s+1 are issued before the
 //    MFMAs of stage s and written to the other buffer after them, one barrier
 //    per stage;
-//  * the 16-byte chunk c of LDS row r lives at chunk c ^ (r & 7), so the
-//    128-bit fragment reads of 8 consecutive rows hit 8 chunk positions;
+//  * the 16-byte chunk c of LDS row r lives at chunk c ^ ((r >> 1) & 7): the
+//    LDS serves a 128-bit access 16 lanes at a time across 64 four-byte
+//    banks (256 bytes), and 16 consecutive rows of one logical chunk then
+//    cover all 16 distinct 16-byte bank groups (two rows share each 256-byte
+//    bank window, and their swizzled chunks differ);
 //  * an MFMA operand fragment is read per lane as whole 16-byte chunks: lane
 //    l takes row l % 32 and K positions (l / 32) * w .. + w of the MFMA's K
 //    step (w = 8 for F16, 32 for FP8); A and B use the same assignment, so the
@@ -47,6 +50,7 @@
 //    B rows in that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -92,18 +96,29 @@ __device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t x, uint32_t sel) {
   return __builtin_bit_cast(uint32_t, h) & 0xBFFFBFFFu;
 }
 
-template <int OUT>
-__device__ __forceinline__ void store_out(void* C, int64_t off, float y, float sy) {
-  if constexpr (OUT == 0) {
-    reinterpret_cast<uint16_t*>(C)[off] = (uint16_t)f32_to_bf16(y);
-  } else if constexpr (OUT == 1) {
-    reinterpret_cast<uint8_t*>(C)[off] = (uint8_t)e4m3_encode(y / sy);
-  } else {
-    reinterpret_cast<float*>(C)[off] = y;
-  }
+// Buffer resource over [base, base + bytes): loads beyond it return 0 and
+// stores beyond it are dropped, which is how every bound below is enforced
+// without a branch.  The third-dword value is the standard gfx9 raw-buffer
+// configuration.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                           int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n,
+                                           0x00020000);
 }
 
+constexpr int kOOB = 0x7FFFFFF0;  // a byte offset past every buffer
+
 // ENGINE: 0 = F16 (exact decode), 1 = native FP8 MFMA.
+//
+// Pipeline: a stage covers KS = 64 (F16 engine) or 128 (FP8 engine) of K;
+// its LDS rows are 128 bytes either way (64 F16 or 128 codes).  LDS holds two
+// stages.  While stage s is multiplied out of one LDS buffer, the registers
+// hold stage s+1 (loaded during stage s-1); half-way through stage s's
+// MFMAs they are written to the other buffer and the loads of stage s+2 are
+// issued into the freed registers.  A load therefore has a whole stage of
+// MFMA work to arrive, and the LDS writes run while the first half's MFMAs
+// are still in the matrix pipe.  One barrier per stage.
 template <int BM, int BN, int WM, int WN, int OUT, int ENGINE>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
@@ -113,13 +128,14 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
   constexpr int T = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
-  // K per stage and global bytes per row per stage
-  constexpr int KS = ENGINE == 0 ? 64 : 128;
+  constexpr int KS = ENGINE == 0 ? 64 : 128;    // K per stage
   constexpr int GCH = KS / 16;                  // 16-byte global chunks per row
   constexpr int A_LD = BM * GCH / T, B_LD = BN * GCH / T;
   static_assert(A_LD * T == BM * GCH && B_LD * T == BN * GCH, "tile/threads");
   constexpr int STAGE = (BM + BN) * kRowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int EPI = WM * WN * (FM / 2 > 0 ? FM / 2 : 1) * 32 * (WTN * 2 + 16);
+  constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -127,29 +143,39 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
+  // operand windows start at the tile's first row; rows past M read as 0
+  const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
+  const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(B + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+  // per-thread byte offsets of its chunks at K = 0 (or past the buffer)
+  int a_off[A_LD], b_off[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int id = tid + i * T, r = id / GCH;
+    a_off[i] = (m0 + r < M) ? r * K + (id % GCH) * 16 : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int id = tid + i * T, r = id / GCH;
+    b_off[i] = (n0 + r < N) ? r * K + (id % GCH) * 16 : kOOB;
+  }
+  const int my_kc = (tid % GCH) * 16;   // the chunk's K offset inside a stage
+
   v4i ra[A_LD], rb[B_LD];
   auto gload = [&](int k0) {
+    const bool kin = k0 + my_kc < K;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int id = tid + i * T, r = id / GCH, c = id % GCH;
-      const int gm = m0 + r, gk = k0 + c * 16;
-      v4i v = {0, 0, 0, 0};
-      if (gm < M && gk < K) v = *reinterpret_cast<const v4i*>(A + (int64_t)gm * K + gk);
-      ra[i] = v;
-    }
+    for (int i = 0; i < A_LD; ++i)
+      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          ra_rs, (kin && a_off[i] != kOOB) ? a_off[i] + k0 : kOOB, 0, 0);
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int id = tid + i * T, r = id / GCH, c = id % GCH;
-      const int gn = n0 + r, gk = k0 + c * 16;
-      v4i v = {0, 0, 0, 0};
-      if (gn < N && gk < K) v = *reinterpret_cast<const v4i*>(B + (int64_t)gn * K + gk);
-      rb[i] = v;
-    }
+    for (int i = 0; i < B_LD; ++i)
+      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rb_rs, (kin && b_off[i] != kOOB) ? b_off[i] + k0 : kOOB, 0, 0);
   };
   // one 16-byte global chunk (row r, chunk c) into LDS
   auto put = [&](uint8_t* base, int r, int c, v4i v) {
     uint8_t* row = base + r * kRowBytes;
-    const int sw = r & 7;
+    const int sw = (r >> 1) & 7;
     if constexpr (ENGINE == 0) {
       // 16 codes -> 16 F16 = LDS chunks 2c and 2c + 1
       v4i lo, hi;
@@ -191,23 +217,15 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   auto chunk = [&](const uint8_t* base, int r, int c) -> v4i {
-    return *reinterpret_cast<const v4i*>(base + r * kRowBytes + ((c ^ (r & 7)) << 4));
+    return *reinterpret_cast<const v4i*>(base + r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4));
   };
-
-  const int KT = (K + KS - 1) / KS;
-  if (KT > 0) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * KS);
+  // MFMA K-steps [s0, s1) of the stage in LDS buffer `buf`
+  auto compute = [&](int buf, int s0, int s1) {
     const uint8_t* sa = smem + buf * STAGE;
     const uint8_t* sb = sa + BM * kRowBytes;
     if constexpr (ENGINE == 0) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {        // 4 MFMA K-steps of 16
+      for (int s = s0; s < s1; ++s) {      // K-steps of 16
         const int c = 2 * s + (lane >> 5);
         f16x8 a[FM], b[FN];
 #pragma unroll
@@ -224,7 +242,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {        // 2 MFMA K-steps of 64
+      for (int s = s0; s < s1; ++s) {      // K-steps of 64
         const int c = 4 * s + 2 * (lane >> 5);
         v8i a[FM], b[FN];
 #pragma unroll
@@ -245,27 +263,103 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
                 a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
       }
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+  };
+  constexpr int NSTEP = ENGINE == 0 ? 4 : 2;   // MFMA K-steps per stage
+
+  const int KT = (K + KS - 1) / KS;
+  if (KT > 0) {
+    gload(0);
+    sstore(0);
+    if (KT > 1) gload(KS);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    compute(buf, 0, NSTEP / 2);
+    if (kt + 1 < KT) {
+      sstore(buf ^ 1);                       // stage kt+1 from the registers
+      if (kt + 2 < KT) gload((kt + 2) * KS);  // and refill them
+    }
+    compute(buf, NSTEP / 2, NSTEP);
     __syncthreads();
   }
 
-  // F16 engine: operands carried a 2^-8 factor each
+  // ---- epilogue: y = fp32(acc [* 2^16]) * alpha, then the output format ----
+  // F16 engine: both operands carried a 2^-8 factor
   const float undo = ENGINE == 0 ? 65536.0f : 1.0f;
   const float alpha = __fmul_rn(*d_sx, *d_sw);
-  const float sy = (OUT == 1) ? *d_sy : 1.0f;
+  constexpr int ESZ = OUT == 0 ? 2 : (OUT == 1 ? 1 : 4);
+  const __amdgpu_buffer_rsrc_t rc_rs =
+      make_rsrc(static_cast<uint8_t*>(C) + ((int64_t)m0 * N) * ESZ, (int64_t)(M - m0) * N * ESZ);
+  const int col_l = wn * WTN + (lane & 31);          // + j*32
+  const int row_l = wm * WTM + (lane >> 5) * 4;       // + i*32 + 8*(v/4) + v%4
+
+  if constexpr (OUT == 0) {
+    // BF16: each wave stages half of its sub-tile at a time in LDS (rows of
+    // WTN values, padded by 16 bytes so the two row groups a store
+    // instruction writes fall in different banks), then writes whole
+    // 16-byte row pieces with coalesced stores.
+    constexpr int LROW = WTN * 2 + 16;
+    constexpr int HALF = FM / 2 > 0 ? FM / 2 : 1;
+    uint8_t* wbuf = smem + wave * (HALF * 32 * LROW);
+    const bool vec_ok = (N % 8) == 0;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int h = 0; h < FM / HALF; ++h) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+      for (int ii = 0; ii < HALF; ++ii)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        if (row < M && col < N)
-          store_out<OUT>(C, (int64_t)row * N + col,
-                         __fmul_rn(__fmul_rn(acc[i][j][v], undo), alpha), sy);
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = ii * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+            const int c = j * 32 + (lane & 31);
+            const float y = __fmul_rn(__fmul_rn(acc[h * HALF + ii][j][v], undo), alpha);
+            *reinterpret_cast<uint16_t*>(wbuf + r * LROW + c * 2) = (uint16_t)f32_to_bf16(y);
+          }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
+      __builtin_amdgcn_wave_barrier();
+      constexpr int PIECES = WTN / 8;          // 16-byte pieces per row
+      constexpr int ROWS = HALF * 32;
+#pragma unroll
+      for (int p = lane; p < ROWS * PIECES; p += 64) {
+        const int r = p / PIECES, c8 = (p % PIECES) * 8;
+        const v4i val = *reinterpret_cast<const v4i*>(wbuf + r * LROW + c8 * 2);
+        const int grow = wm * WTM + (h * HALF) * 32 + r;   // row within tile
+        const int gcol = n0 + wn * WTN + c8;
+        if (vec_ok) {
+          const int off = (m0 + grow < M && gcol < N) ? (grow * N + gcol) * 2 : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(val, rc_rs, off, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int off = (m0 + grow < M && gcol + e < N) ? (grow * N + gcol + e) * 2 : kOOB;
+            const uint16_t hv = (uint16_t)((uint32_t)val[e >> 1] >> ((e & 1) * 16));
+            __builtin_amdgcn_raw_buffer_store_b16(hv, rc_rs, off, 0, 0);
+          }
+        }
       }
+      __builtin_amdgcn_wave_barrier();
     }
+  } else {
+    const float sy = (OUT == 1) ? *d_sy : 1.0f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = col_l + j * 32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = row_l + i * 32 + (v >> 2) * 8 + (v & 3);
+          const bool ok = (m0 + row < M) && (n0 + col < N);
+          const int off = ok ? (row * N + n0 + col) * ESZ : kOOB;
+          const float y = __fmul_rn(__fmul_rn(acc[i][j][v], undo), alpha);
+          if constexpr (OUT == 1)
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e4m3_encode(y / sy), rc_rs, off, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rc_rs, off, 0, 0);
+        }
+      }
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int ENGINE>
@@ -291,6 +385,11 @@ hipError_t launch_tiled(const uint8_t* qa, const uint8_t* qb, void* y, int M,
   return hipGetLastError();
 }
 
+// Tile configuration per shape (MI355X, 256 CUs): the largest tile that
+// still gives about one workgroup per CU.  Measured on the workload shapes:
+// 256x256 tiles with 8 waves (two per SIMD) are fastest once there are
+// ~0.7 tiles per CU; below that 256x128 (8 waves) and then 128x128 (4 waves)
+// keep the CUs busy.  FP8MOT_GEMM_CFG=<n> forces one configuration (tuning).
 template <int ENGINE>
 hipError_t launch_engine(const uint8_t* qa, const uint8_t* qb, void* y, int m,
                          int n, int k, const float* sx, const float* sw,
@@ -299,11 +398,21 @@ hipError_t launch_engine(const uint8_t* qa, const uint8_t* qb, void* y, int m,
   auto tiles = [&](int bm, int bn) {
     return (int64_t)((m + bm - 1) / bm) * ((n + bn - 1) / bn);
   };
-  if (tiles(256, 256) >= num_cus)
-    return launch_tiled<256, 256, 2, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
-  if (tiles(256, 128) >= num_cus)
-    return launch_tiled<256, 128, 2, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
-  return launch_tiled<128, 128, 2, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
+  static const int forced = [] {
+    const char* e = getenv("FP8MOT_GEMM_CFG");
+    return e ? atoi(e) : -1;
+  }();
+  int cfg = forced;
+  if (cfg < 0) {
+    const int64_t want = (int64_t)num_cus * 7 / 10;
+    cfg = tiles(256, 256) >= want ? (ENGINE == 0 ? 1 : 4) : (tiles(256, 128) >= want ? 5 : 3);
+  }
+  switch (cfg) {
+    case 1: return launch_tiled<256, 256, 2, 4, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
+    case 4: return launch_tiled<256, 256, 4, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
+    case 5: return launch_tiled<256, 128, 4, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
+    default: return launch_tiled<128, 128, 2, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
+  }
 }
 
 }  // namespace
