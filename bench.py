@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="rows of X in the oracle's timed sample")
+    p.add_argument("--copy-calib-mb", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (a "
+                        "known-size reference for the profiler's byte counters)")
     return p.parse_args()
 
 
@@ -119,31 +122,30 @@ def main():
     names = ["quant", "gate", "up", "silu", "down"]
 
     def per_kernel(accum):
-        # all repetitions are enqueued back to back (no host sync in between)
-        # so the GPU never idles waiting for a launch; events bracket each
-        # kernel on the stream it runs on
+        # average launch time of each kernel of the step: `reps` launches of
+        # that kernel back to back on the stream, bracketed by one pair of
+        # HIP events on that stream (no host sync, no event between them)
         reps = max(args.steps, 10)
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
-               for _ in range(reps + 2)]
-        for r in range(reps + 2):
-            ev = evs[r]
-            ev[0].record(stream)
-            fp8.fp8_quant_static(x, sx, out=qxb)
-            ev[1].record(stream)
-            fp8.fp8_linear(qxb, q["gate"], sx, s["gate"], out=Gb, accum=accum)
-            ev[2].record(stream)
-            fp8.fp8_linear(qxb, q["up"], sx, s["up"], out=Ub, accum=accum)
-            ev[3].record(stream)
-            fp8.silu_mul_2in_fp8(Gb, Ub, sh, out=qh)
-            ev[4].record(stream)
-            fp8.fp8_linear(qh, q["down"], sh, s["down"], out=y, accum=accum)
-            ev[5].record(stream)
-        torch.cuda.synchronize()
-        acc = {n: 0.0 for n in names}
-        for r in range(2, reps + 2):
-            for i, n in enumerate(names):
-                acc[n] += evs[r][i].elapsed_time(evs[r][i + 1])
-        return {n: acc[n] / reps * 1e3 for n in names}
+        calls = {
+            "quant": lambda: fp8.fp8_quant_static(x, sx, out=qxb),
+            "gate": lambda: fp8.fp8_linear(qxb, q["gate"], sx, s["gate"], out=Gb, accum=accum),
+            "up": lambda: fp8.fp8_linear(qxb, q["up"], sx, s["up"], out=Ub, accum=accum),
+            "silu": lambda: fp8.silu_mul_2in_fp8(Gb, Ub, sh, out=qh),
+            "down": lambda: fp8.fp8_linear(qh, q["down"], sh, s["down"], out=y, accum=accum),
+        }
+        out = {}
+        for n in names:
+            for _ in range(3):
+                calls[n]()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                calls[n]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[n] = e0.elapsed_time(e1) / reps * 1e3
+        return out
 
     us = per_kernel(fp8.ACC_EXACT)
     us8 = per_kernel(fp8.ACC_FP8_MFMA)
@@ -171,7 +173,7 @@ def main():
         "kernel": f"gemm (exact engine, f16 MFMA) {M}x{I}x{H} gate/up",
         "bound": "mfma", "achieved": gate_tflops, "peak": F16_PEAK_TFLOPS,
         "unit": "TFLOP/s", "frac": gate_tflops / F16_PEAK_TFLOPS,
-        "traffic": None,
+        "traffic": recorded_traffic(f"gemm_exact_{M}x{I}x{H}"),
     }
     g8 = gate_flops / (us8["gate"] * 1e-6) / 1e12
     fp8_engine = {
@@ -182,6 +184,14 @@ def main():
                      "bound": "mfma", "achieved": g8, "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": g8 / FP8_PEAK_TFLOPS},
     }
+
+    if args.copy_calib_mb > 0:
+        n = args.copy_calib_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -199,6 +209,27 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out))
+
+
+def recorded_traffic(key):
+    """HBM-side bytes per launch of a kernel, as recorded from rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy of known size) in
+    profiles/gemm_traffic.md, or None when that record is missing or was
+    taken from a different version of the GEMM source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.md")
+    src = os.path.join(ROOT, "mlp_fp8_quant_amd", "csrc", "gemm.hip")
+    try:
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        for line in open(path):
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 5 and cells[0] == key and cells[4] == digest:
+                return {"fetch_bytes": float(cells[1]), "write_bytes": float(cells[2]),
+                        "total_bytes": float(cells[1]) + float(cells[2]),
+                        "algorithmic_bytes": float(cells[3])}
+    except (OSError, ValueError):
+        pass
+    return None
 
 
 def cpu_baseline(wl, rows):

@@ -116,7 +116,10 @@ __device__ __forceinline__ void block_max_to(uint32_t v, uint32_t* dst) {
     uint32_t m = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) m = m > red[w] ? m : red[w];
-    atomicMax(dst, m);
+    // only blocks that can raise the running max touch the shared word, so
+    // the atomics do not serialize on one address across the whole grid
+    if (m > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(dst, m);
   }
 }
 
@@ -231,6 +234,8 @@ hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
 hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,
                           fp8mot_observer_state_dev* st, int mode, float c,
                           int max_blocks, hipStream_t stream) {
+  // a reduction needs few blocks: two per CU, each striding over the input
+  max_blocks = max_blocks / 4 > 0 ? max_blocks / 4 : 1;
   if (u == nullptr) {
     hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid_for(n >> 3, max_blocks)),
                        dim3(kThreads), 0, stream, x, n, &st->pending);
