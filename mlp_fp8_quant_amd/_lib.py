@@ -30,6 +30,9 @@ SIGNATURES = {
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_int, c_void_p]),
+    "fp8_gate_up_swiglu": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64,
+                                   c_int, c_void_p]),
     "qkv_fp8_workspace": (c_size_t, [c_i64, c_i64]),
     "qkv_fp8": (c_int, [c_void_p, c_i64, c_i64, c_void_p,
                         c_void_p, c_i64, c_void_p, c_void_p, c_i64, c_void_p,

@@ -114,6 +114,31 @@ def silu_mul_2in_fp8(g, u, s_out, out=None):
     return out
 
 
+def fp8_gate_up_swiglu(qx, wg, sx, sg, wu, su, sh, out=None, accum=ACC_EXACT):
+    """qh = SwiGLU-FP8 of the gate and up projections of an E4M3 activation
+    qx [..., H] (wg, wu [I, H]); bitwise what fp8_linear (BF16 out) twice and
+    silu_mul_2in_fp8 give, in one kernel."""
+    _need(qx, "qx", torch.uint8)
+    dev = qx.device
+    _need(wg, "wg", torch.uint8, dev)
+    _need(wu, "wu", torch.uint8, dev)
+    H = qx.shape[-1]
+    I = wg.shape[0]
+    if wg.shape != (I, H) or wu.shape != (I, H):
+        raise ValueError("shapes: qx [..., H]; wg, wu [I, H]")
+    for t, n in ((sx, "sx"), (sg, "sg"), (su, "su"), (sh, "sh")):
+        _scale(t, n, dev)
+    M = math.prod(qx.shape[:-1])
+    if out is None:
+        out = torch.empty((*qx.shape[:-1], I), dtype=torch.uint8, device=dev)
+    _need(out, "out", torch.uint8, dev)
+    if out.numel() != M * I:
+        raise ValueError("out must hold M * I elements")
+    _lib.call("fp8_gate_up_swiglu", _ptr(qx), _ptr(wg), _ptr(sx), _ptr(sg),
+              _ptr(wu), _ptr(su), _ptr(sh), _ptr(out), M, I, H, accum, _stream(qx))
+    return out
+
+
 def gated_mlp_fp8_workspace(M, H, I):
     return int(_lib.lib().gated_mlp_fp8_workspace(M, H, I))
 

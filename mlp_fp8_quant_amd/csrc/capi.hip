@@ -56,15 +56,14 @@ int ew_blocks(int cus) { return cus * 8; }
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct MlpLayout {
-  size_t qx, g, u, qh, total;
+  size_t qx, qh, total;
 };
 
+// qX [M, H] then qH [M, I]; G and U never leave the fused gate/up kernel
 MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I) {
   MlpLayout l;
   l.qx = 0;
-  l.g = l.qx + round256((size_t)M * H);
-  l.u = l.g + round256((size_t)M * I * 2);
-  l.qh = l.u + round256((size_t)M * I * 2);
+  l.qh = l.qx + round256((size_t)M * H);
   l.total = l.qh + round256((size_t)M * I);
   return l;
 }
@@ -174,20 +173,36 @@ int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
   if (st != FP8MOT_OK) return st;
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* qx = base + l.qx;
-  uint16_t* g = reinterpret_cast<uint16_t*>(base + l.g);
-  uint16_t* u = reinterpret_cast<uint16_t*>(base + l.u);
   uint8_t* qh = base + l.qh;
   g_quant_launches.fetch_add(1);
   hipError_t e = launch_quant_static(x, qx, M * H, d_sx, ew_blocks(cus), stream);
+  // gate and up GEMMs with the SwiGLU-FP8 epilogue in one launch: the same
+  // arithmetic, in the same order, as the two BF16 GEMMs and
+  // silu_mul_2in_fp8, without writing G and U
   if (e == hipSuccess && I > 0)
-    e = launch_gemm(qx, wg, g, M, I, H, d_sx, d_sg, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
-  if (e == hipSuccess && I > 0)
-    e = launch_gemm(qx, wu, u, M, I, H, d_sx, d_su, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
-  if (e == hipSuccess && I > 0)
-    e = launch_silu_mul(g, u, qh, M * I, d_sh, ew_blocks(cus), stream);
+    e = launch_gemm_swiglu(qx, wg, wu, qh, M, I, H, d_sx, d_sg, d_su, d_sh, accum, stream);
   if (e == hipSuccess)
     e = launch_gemm(qh, wd, y, M, H, I, d_sh, d_sd, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
   return hip_status(e);
+}
+
+int fp8_gate_up_swiglu(const uint8_t* qx, const uint8_t* wg, const float* d_sx,
+                       const float* d_sg, const uint8_t* wu, const float* d_su,
+                       const float* d_sh, uint8_t* qh, int64_t M, int64_t I,
+                       int64_t H, int accum, hipStream_t stream) {
+  if (!d_sx || !d_sg || !d_su || !d_sh) return FP8MOT_ERR_UNSUPPORTED;
+  if (accum != FP8MOT_ACC_EXACT && accum != FP8MOT_ACC_FP8_MFMA) return FP8MOT_ERR_INVALID_ARG;
+  if (M < 0 || H < 0 || I < 0 || (H % 16) != 0 || (I % 16) != 0)
+    return FP8MOT_ERR_INVALID_ARG;
+  if (M > INT32_MAX || H > INT32_MAX || I > INT32_MAX) return FP8MOT_ERR_INVALID_ARG;
+  if (M == 0 || I == 0) return FP8MOT_OK;
+  if (!qh || (H > 0 && (!qx || !wg || !wu))) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(qx) || !aligned16(wg) || !aligned16(wu) || !aligned16(qh))
+    return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_gemm_swiglu(qx, wg, wu, qh, M, I, H, d_sx, d_sg, d_su, d_sh, accum, stream));
 }
 
 size_t qkv_fp8_workspace(int64_t M, int64_t H) {

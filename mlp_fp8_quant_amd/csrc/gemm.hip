@@ -52,6 +52,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -119,12 +121,27 @@ constexpr int kOOB = 0x7FFFFFF0;  // a byte offset past every buffer
 // issued into the freed registers.  A load therefore has a whole stage of
 // MFMA work to arrive, and the LDS writes run while the first half's MFMAs
 // are still in the matrix pipe.  One barrier per stage.
-template <int BM, int BN, int WM, int WN, int OUT, int ENGINE>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
-    void* __restrict__ C, int M, int N, int K, const float* __restrict__ d_sx,
-    const float* __restrict__ d_sw, const float* __restrict__ d_sy,
-    int tiles_m, int tiles_n) {
+struct GemmArgs {
+  const uint8_t* A;   // [M, K]
+  const uint8_t* B;   // [N, K]   (fused: the gate weight)
+  const uint8_t* B2;  // fused: the up weight [N, K]
+  void* C;            // [M, N]   (fused: the FP8 SwiGLU output)
+  int M, N, K;
+  const float* sx;
+  const float* sw;    // (fused: gate weight scale)
+  const float* sw2;   // fused: up weight scale
+  const float* sy;    // FP8 output scale (fused: the down projection's input scale)
+  int tiles_m, tiles_n;
+};
+
+// OUT: 0 BF16, 1 FP8, 2 FP32.  FUSED: gate and up GEMMs of a gated MLP in one
+// tile (BN = 256 = 128 gate rows + 128 up rows of the same output columns)
+// whose epilogue applies SwiGLU and writes FP8, bit for bit what the separate
+// BF16 GEMMs followed by silu_mul_2in_fp8 produce.
+template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED, int PIPE>
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
+  const uint8_t* __restrict__ A = g.A;
+  const int M = g.M, N = g.N, K = g.K;
   constexpr int T = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
@@ -133,20 +150,27 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
   constexpr int A_LD = BM * GCH / T, B_LD = BN * GCH / T;
   static_assert(A_LD * T == BM * GCH && B_LD * T == BN * GCH, "tile/threads");
   constexpr int STAGE = (BM + BN) * kRowBytes;
-  constexpr int EPI = WM * WN * (FM / 2 > 0 ? FM / 2 : 1) * 32 * (WTN * 2 + 16);
+  static_assert(!FUSED || (BN == 256 && FN % 2 == 0), "fused tiles pair gate/up blocks");
+  constexpr int EPI = FUSED ? WM * WN * WTM * (WTN / 2 + 16)
+                            : WM * WN * (FM / 2 > 0 ? FM / 2 : 1) * 32 * (WTN * 2 + 16);
   constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  // output columns of this tile start at n0 (fused: 128 of each of G and U)
+  const int m0 = tm * BM, n0 = tn * (FUSED ? BN / 2 : BN);
 
   // operand windows start at the tile's first row; rows past M read as 0
   const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
-  const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(B + (int64_t)n0 * K, (int64_t)(N - n0) * K);
-  // per-thread byte offsets of its chunks at K = 0 (or past the buffer)
+  const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(g.B + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+  const __amdgpu_buffer_rsrc_t rb2_rs =
+      FUSED ? make_rsrc(g.B2 + (int64_t)n0 * K, (int64_t)(N - n0) * K) : rb_rs;
+  // per-thread byte offsets of its chunks at K = 0 (or past the buffer).
+  // Fused: load rows 0..127 are gate rows, 128..255 the up rows of the same
+  // output columns (chunk index i < B_LD / 2 is gate, the rest up).
   int a_off[A_LD], b_off[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
@@ -155,7 +179,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int id = tid + i * T, r = id / GCH;
+    const int id = tid + i * T, r = (id / GCH) % (FUSED ? BN / 2 : BN);
     b_off[i] = (n0 + r < N) ? r * K + (id % GCH) * 16 : kOOB;
   }
   const int my_kc = (tid % GCH) * 16;   // the chunk's K offset inside a stage
@@ -170,7 +194,18 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < B_LD; ++i)
       rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rb_rs, (kin && b_off[i] != kOOB) ? b_off[i] + k0 : kOOB, 0, 0);
+          (FUSED && i >= B_LD / 2) ? rb2_rs : rb_rs,
+          (kin && b_off[i] != kOOB) ? b_off[i] + k0 : kOOB, 0, 0);
+  };
+  // LDS row of B load row r.  Fused: 32-row blocks alternate gate / up, so a
+  // wave's 32x32 blocks j (gate) and j + 1 (up) cover the same columns.
+  auto b_row = [&](int r) -> int {
+    if constexpr (FUSED) {
+      const int q = r & 127;
+      return 64 * (q >> 5) + (r >= 128 ? 32 : 0) + (q & 31);
+    } else {
+      return r;
+    }
   };
   // one 16-byte global chunk (row r, chunk c) into LDS
   auto put = [&](uint8_t* base, int r, int c, v4i v) {
@@ -204,7 +239,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int id = tid + i * T;
-      put(sb, id / GCH, id % GCH, rb[i]);
+      put(sb, b_row(id / GCH), id % GCH, rb[i]);
     }
   };
 
@@ -219,82 +254,159 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
   auto chunk = [&](const uint8_t* base, int r, int c) -> v4i {
     return *reinterpret_cast<const v4i*>(base + r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4));
   };
-  // MFMA K-steps [s0, s1) of the stage in LDS buffer `buf`
-  auto compute = [&](int buf, int s0, int s1) {
+  constexpr int NSTEP = ENGINE == 0 ? 4 : 2;   // MFMA K-steps per stage
+  // operand fragments, double-buffered: K-step s of a stage uses slot s & 1
+  // (NSTEP is even, so the slot of step s is the same in every stage)
+  typedef typename std::conditional<ENGINE == 0, f16x8, v8i>::type frag_t;
+  frag_t fa[2][FM], fb[2][FN];
+  auto rd = [&](int buf, int s, int slot) {   // fragments of K-step s
     const uint8_t* sa = smem + buf * STAGE;
     const uint8_t* sb = sa + BM * kRowBytes;
     if constexpr (ENGINE == 0) {
+      const int c = 2 * s + (lane >> 5);
 #pragma unroll
-      for (int s = s0; s < s1; ++s) {      // K-steps of 16
-        const int c = 2 * s + (lane >> 5);
-        f16x8 a[FM], b[FN];
+      for (int i = 0; i < FM; ++i)
+        fa[slot][i] = __builtin_bit_cast(f16x8, chunk(sa, wm * WTM + i * 32 + (lane & 31), c));
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          a[i] = __builtin_bit_cast(f16x8, chunk(sa, wm * WTM + i * 32 + (lane & 31), c));
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          b[j] = __builtin_bit_cast(f16x8, chunk(sb, wn * WTN + j * 32 + (lane & 31), c));
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
+      for (int j = 0; j < FN; ++j)
+        fb[slot][j] = __builtin_bit_cast(f16x8, chunk(sb, wn * WTN + j * 32 + (lane & 31), c));
     } else {
+      const int c = 4 * s + 2 * (lane >> 5);
 #pragma unroll
-      for (int s = s0; s < s1; ++s) {      // K-steps of 64
-        const int c = 4 * s + 2 * (lane >> 5);
-        v8i a[FM], b[FN];
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WTM + i * 32 + (lane & 31);
+        fa[slot][i] = __builtin_shufflevector(chunk(sa, r, c), chunk(sa, r, c + 1), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * WTM + i * 32 + (lane & 31);
-          a[i] = __builtin_shufflevector(chunk(sa, r, c), chunk(sa, r, c + 1), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int r = wn * WTN + j * 32 + (lane & 31);
-          b[j] = __builtin_shufflevector(chunk(sb, r, c), chunk(sb, r, c + 1), 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WTN + j * 32 + (lane & 31);
+        fb[slot][j] = __builtin_shufflevector(chunk(sb, r, c), chunk(sb, r, c + 1), 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
   };
-  constexpr int NSTEP = ENGINE == 0 ? 4 : 2;   // MFMA K-steps per stage
+  auto mf = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (ENGINE == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+      }
+  };
 
+  // Software pipeline, per stage kt (LDS buffer kt & 1):
+  //  step 0:        issue the fragment reads of step 1, write stage kt+1 from
+  //                 the registers into the other LDS buffer and refill the
+  //                 registers with the loads of stage kt+2, then the MFMAs of
+  //                 step 0 (their fragments were read one step earlier);
+  //  steps 1..n-2:  fragment reads of the next step, MFMAs of this step;
+  //  step n-1:      barrier (every wave has written stage kt+1 and read all
+  //                 of stage kt), fragment reads of stage kt+1 step 0 from the
+  //                 other buffer, MFMAs of step n-1.
   const int KT = (K + KS - 1) / KS;
-  if (KT > 0) {
-    gload(0);
-    sstore(0);
-    if (KT > 1) gload(KS);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    compute(buf, 0, NSTEP / 2);
-    if (kt + 1 < KT) {
-      sstore(buf ^ 1);                       // stage kt+1 from the registers
-      if (kt + 2 < KT) gload((kt + 2) * KS);  // and refill them
+  if constexpr (PIPE == 1) {
+    if (KT > 0) {
+      gload(0);
+      sstore(0);
+      if (KT > 1) gload(KS);
+      __syncthreads();
+      rd(0, 0, 0);
     }
-    compute(buf, NSTEP / 2, NSTEP);
-    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt & 1;
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + 1 < NSTEP) {
+          rd(buf, st + 1, (st + 1) & 1);
+        } else if (kt + 1 < KT) {
+          __syncthreads();
+          rd(buf ^ 1, 0, 0);
+        }
+        if (st == 0 && kt + 1 < KT) {
+          sstore(buf ^ 1);
+          if (kt + 2 < KT) gload((kt + 2) * KS);
+        }
+        mf(st & 1);
+      }
+    }
+  } else {
+    // single fragment set (for register-heavy tiles): each K-step reads its
+    // fragments and multiplies; the next stage is written to LDS and the one
+    // after it loaded half-way through the stage
+    if (KT > 0) {
+      gload(0);
+      sstore(0);
+      if (KT > 1) gload(KS);
+      __syncthreads();
+    }
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt & 1;
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st == NSTEP / 2 && kt + 1 < KT) {
+          sstore(buf ^ 1);
+          if (kt + 2 < KT) gload((kt + 2) * KS);
+        }
+        rd(buf, st, 0);
+        mf(0);
+      }
+      __syncthreads();
+    }
   }
+  __syncthreads();
 
   // ---- epilogue: y = fp32(acc [* 2^16]) * alpha, then the output format ----
   // F16 engine: both operands carried a 2^-8 factor
   const float undo = ENGINE == 0 ? 65536.0f : 1.0f;
-  const float alpha = __fmul_rn(*d_sx, *d_sw);
+  const float alpha = __fmul_rn(*g.sx, *g.sw);
+  void* __restrict__ C = g.C;
   constexpr int ESZ = OUT == 0 ? 2 : (OUT == 1 ? 1 : 4);
   const __amdgpu_buffer_rsrc_t rc_rs =
       make_rsrc(static_cast<uint8_t*>(C) + ((int64_t)m0 * N) * ESZ, (int64_t)(M - m0) * N * ESZ);
   const int col_l = wn * WTN + (lane & 31);          // + j*32
   const int row_l = wm * WTM + (lane >> 5) * 4;       // + i*32 + 8*(v/4) + v%4
 
-  if constexpr (OUT == 0) {
+  if constexpr (FUSED) {
+    // G and U of one output element sit in blocks j (gate) and j + 1 (up) of
+    // the same lane and register: round each to BF16 exactly as the BF16
+    // epilogue does, apply SwiGLU exactly as silu_mul_2in_fp8 does, stage the
+    // codes of the wave's [WTM x WTN/2] piece in LDS and store 16-byte rows.
+    const float alpha_u = __fmul_rn(*g.sx, *g.sw2);
+    const float rs = 1.0f / *g.sy;
+    constexpr int QW = WTN / 2;            // output columns per wave
+    constexpr int LROW = QW + 16;
+    uint8_t* wbuf = smem + wave * (WTM * LROW);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int p = 0; p < FN / 2; ++p)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int c = p * 32 + (lane & 31);
+          const float yg = __fmul_rn(__fmul_rn(acc[i][2 * p][v], undo), alpha);
+          const float yu = __fmul_rn(__fmul_rn(acc[i][2 * p + 1][v], undo), alpha_u);
+          const float h = silu_mul(bf16_to_f32(f32_to_bf16(yg)), bf16_to_f32(f32_to_bf16(yu)));
+          wbuf[r * LROW + c] = (uint8_t)e4m3_encode(__fmul_rn(h, rs));
+        }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    constexpr int PIECES = QW / 16;
+    const __amdgpu_buffer_rsrc_t rq_rs =
+        make_rsrc(static_cast<uint8_t*>(C) + (int64_t)m0 * N, (int64_t)(M - m0) * N);
+#pragma unroll
+    for (int p = lane; p < WTM * PIECES; p += 64) {
+      const int r = p / PIECES, c16 = (p % PIECES) * 16;
+      const v4i val = *reinterpret_cast<const v4i*>(wbuf + r * LROW + c16);
+      const int grow = wm * WTM + r;                           // row within tile
+      const int gcol = n0 + (wn * WTN) / 2 + c16;              // output column
+      const int off = (m0 + grow < M && gcol < N) ? grow * N + gcol : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(val, rq_rs, off, 0, 0);
+    }
+  } else if constexpr (OUT == 0) {
     // BF16: each wave stages half of its sub-tile at a time in LDS (rows of
     // WTN values, padded by 16 bytes so the two row groups a store
     // instruction writes fall in different banks), then writes whole
@@ -341,7 +453,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
       __builtin_amdgcn_wave_barrier();
     }
   } else {
-    const float sy = (OUT == 1) ? *d_sy : 1.0f;
+    const float sy = (OUT == 1) ? *g.sy : 1.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -362,26 +474,36 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(
   }
 }
 
+// Pipeline style: double-buffered fragments (1) except for the FP8 engine with
+// 8 waves, whose 32-byte fragments would not fit twice in 256 registers (0).
+template <int ENGINE, int WAVES>
+constexpr int kPipe = (ENGINE == 1 && WAVES == 8) ? 0 : 1;
+
 template <int BM, int BN, int WM, int WN, int ENGINE>
-hipError_t launch_tiled(const uint8_t* qa, const uint8_t* qb, void* y, int M,
-                        int N, int K, const float* sx, const float* sw,
-                        int out_kind, const float* sy, hipStream_t stream) {
-  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  const dim3 grid(tm * tn), block(WM * WN * 64);
+hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
   switch (out_kind) {
     case 0:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE>), grid, block, 0,
-                         stream, qa, qb, y, M, N, K, sx, sw, sy, tm, tn);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE, false, kPipe<ENGINE, WM * WN>>), grid, block, 0, stream, a);
       break;
     case 1:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE>), grid, block, 0,
-                         stream, qa, qb, y, M, N, K, sx, sw, sy, tm, tn);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false, kPipe<ENGINE, WM * WN>>), grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE>), grid, block, 0,
-                         stream, qa, qb, y, M, N, K, sx, sw, sy, tm, tn);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false, kPipe<ENGINE, WM * WN>>), grid, block, 0, stream, a);
       break;
   }
+  return hipGetLastError();
+}
+
+template <int BM, int WM, int WN, int ENGINE>
+hipError_t launch_fused(GemmArgs a, hipStream_t stream) {
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + 127) / 128;
+  const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+  hipLaunchKernelGGL((gemm_kernel<BM, 256, WM, WN, 0, ENGINE, true, kPipe<ENGINE, WM * WN>>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -391,12 +513,9 @@ hipError_t launch_tiled(const uint8_t* qa, const uint8_t* qb, void* y, int M,
 // ~0.7 tiles per CU; below that 256x128 (8 waves) and then 128x128 (4 waves)
 // keep the CUs busy.  FP8MOT_GEMM_CFG=<n> forces one configuration (tuning).
 template <int ENGINE>
-hipError_t launch_engine(const uint8_t* qa, const uint8_t* qb, void* y, int m,
-                         int n, int k, const float* sx, const float* sw,
-                         int out_kind, const float* sy, int num_cus,
-                         hipStream_t stream) {
+hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stream) {
   auto tiles = [&](int bm, int bn) {
-    return (int64_t)((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+    return (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
   };
   static const int forced = [] {
     const char* e = getenv("FP8MOT_GEMM_CFG");
@@ -405,13 +524,14 @@ hipError_t launch_engine(const uint8_t* qa, const uint8_t* qb, void* y, int m,
   int cfg = forced;
   if (cfg < 0) {
     const int64_t want = (int64_t)num_cus * 7 / 10;
-    cfg = tiles(256, 256) >= want ? (ENGINE == 0 ? 1 : 4) : (tiles(256, 128) >= want ? 5 : 3);
+    cfg = tiles(256, 256) >= want ? 1 : (tiles(256, 128) >= want ? 5 : 3);
   }
   switch (cfg) {
-    case 1: return launch_tiled<256, 256, 2, 4, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
-    case 4: return launch_tiled<256, 256, 4, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
-    case 5: return launch_tiled<256, 128, 4, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
-    default: return launch_tiled<128, 128, 2, 2, ENGINE>(qa, qb, y, m, n, k, sx, sw, out_kind, sy, stream);
+    case 0: return launch_tiled<256, 256, 2, 2, ENGINE>(a, out_kind, stream);
+    case 1: return launch_tiled<256, 256, 2, 4, ENGINE>(a, out_kind, stream);
+    case 4: return launch_tiled<256, 256, 4, 2, ENGINE>(a, out_kind, stream);
+    case 5: return launch_tiled<256, 128, 4, 2, ENGINE>(a, out_kind, stream);
+    default: return launch_tiled<128, 128, 2, 2, ENGINE>(a, out_kind, stream);
   }
 }
 
@@ -421,9 +541,18 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        int64_t M, int64_t N, int64_t K, const float* sx,
                        const float* sw, int out_kind, const float* sy,
                        int accum, int num_cus, hipStream_t stream) {
-  if (accum == 1)
-    return launch_engine<1>(qa, qb, y, (int)M, (int)N, (int)K, sx, sw, out_kind, sy, num_cus, stream);
-  return launch_engine<0>(qa, qb, y, (int)M, (int)N, (int)K, sx, sw, out_kind, sy, num_cus, stream);
+  GemmArgs a{qa, qb, nullptr, y, (int)M, (int)N, (int)K, sx, sw, nullptr, sy, 0, 0};
+  if (accum == 1) return launch_engine<1>(a, out_kind, num_cus, stream);
+  return launch_engine<0>(a, out_kind, num_cus, stream);
+}
+
+hipError_t launch_gemm_swiglu(const uint8_t* qx, const uint8_t* wg, const uint8_t* wu,
+                              uint8_t* qh, int64_t M, int64_t I, int64_t H,
+                              const float* sx, const float* sg, const float* su,
+                              const float* sh, int accum, hipStream_t stream) {
+  GemmArgs a{qx, wg, wu, qh, (int)M, (int)I, (int)H, sx, sg, su, sh, 0, 0};
+  if (accum == 1) return launch_fused<256, 2, 4, 1>(a, stream);
+  return launch_fused<256, 2, 4, 0>(a, stream);
 }
 
 }  // namespace fp8mot

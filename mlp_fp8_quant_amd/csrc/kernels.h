@@ -12,8 +12,8 @@ namespace fp8mot {
 struct fp8mot_observer_state_dev {
   float m;
   int32_t count;
-  uint32_t pending;  // FP32 bit pattern of the running amax of the current call
-  uint32_t reserved;
+  uint32_t pending;   // FP32 bit pattern of the running amax of the current call
+  uint32_t arrivals;  // blocks of the current call that have finished
 };
 
 hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
@@ -38,5 +38,13 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        int64_t M, int64_t N, int64_t K, const float* sx,
                        const float* sw, int out_kind, const float* sy,
                        int accum, int num_cus, hipStream_t stream);
+
+// Gate and up GEMMs of a gated MLP with the SwiGLU-FP8 epilogue in one launch:
+// qh[M,I] = e4m3(silu(bf16(G)) * bf16(U) / sh) with G = qx.wg^T * (sx*sg),
+// U = qx.wu^T * (sx*su); bitwise equal to two BF16 GEMMs + launch_silu_mul.
+hipError_t launch_gemm_swiglu(const uint8_t* qx, const uint8_t* wg, const uint8_t* wu,
+                              uint8_t* qh, int64_t M, int64_t I, int64_t H,
+                              const float* sx, const float* sg, const float* su,
+                              const float* sh, int accum, hipStream_t stream);
 
 }  // namespace fp8mot

@@ -30,7 +30,7 @@ def test_header_declares_the_hot_path_calls():
     names = declared_functions()
     for n in ("fp8_quant_static", "fp8_linear", "silu_mul_2in_fp8",
               "gated_mlp_fp8", "qkv_fp8", "fp8_observe", "fp8_scale_from_state",
-              "fp8_check_shared_scale"):
+              "fp8_check_shared_scale", "fp8_gate_up_swiglu"):
         assert n in names
 
 
@@ -67,7 +67,7 @@ def test_workspace_sizes():
     lib = _lib()
     M, H, I = 2048, 2048, 8192
     r = lambda b: (b + 255) // 256 * 256  # noqa: E731
-    assert lib.gated_mlp_fp8_workspace(M, H, I) == r(M * H) + 2 * r(2 * M * I) + r(M * I)
+    assert lib.gated_mlp_fp8_workspace(M, H, I) == r(M * H) + r(M * I)
     assert lib.qkv_fp8_workspace(3072, 4096) == 3072 * 4096
     assert lib.gated_mlp_fp8_workspace(-1, 1, 1) == 0
 
@@ -108,6 +108,10 @@ def test_refusals_before_any_device_access():
                              fake, null, 0, 0, null) == 6
     assert lib.gated_mlp_fp8(fake, 4, 16, 32, null, fake, s, fake, s, s, fake, s,
                              fake, fake, 1 << 20, 0, null) == 4
+    assert lib.fp8_gate_up_swiglu(fake, fake, s, s, fake, s, null, fake, 4, 32, 16, 0, null) == 4
+    assert lib.fp8_gate_up_swiglu(fake, fake, s, s, fake, s, s, fake, 4, 24, 16, 0, null) == 1
+    assert lib.fp8_gate_up_swiglu(fake, odd, s, s, fake, s, s, fake, 4, 32, 16, 0, null) == 2
+    assert lib.fp8_gate_up_swiglu(null, null, s, s, null, s, s, null, 0, 32, 16, 0, null) == 0
     # unknown accumulation engine -> INVALID_ARG
     assert lib.fp8_linear(fake, fake, fake, 4, 4, 16, s, s, 0, null, 2, null) == 1
     assert lib.gated_mlp_fp8(fake, 4, 16, 32, s, fake, s, fake, s, s, fake, s,

@@ -109,6 +109,8 @@ def test_gated_mlp_composite_equals_parts_and_oracle():
     qh = fp8.silu_mul_2in_fp8(G, U, dsh)
     y2 = fp8.fp8_linear(qh, c["d"]["down"], dsh, c["sc"]["down"])
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(fp8.fp8_gate_up_swiglu(qx, c["d"]["gate"], dsx, c["sc"]["gate"],
+                                              c["d"]["up"], c["sc"]["up"], dsh), qh)
     # stage-wise against the oracle
     assert np.array_equal(host_u8(qx), c["qx"])
     Gb = host_bits(G)
@@ -228,8 +230,32 @@ def test_composites_equal_parts_each_engine(accum):
     y2 = fp8.fp8_linear(fp8.silu_mul_2in_fp8(G, U, dsh), d["d"], dsh, sc["d"],
                         accum=accum)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    qh = fp8.fp8_gate_up_swiglu(qx, d["g"], dsx, sc["g"], d["u"], sc["u"], dsh,
+                                accum=accum)
+    assert torch.equal(qh, fp8.silu_mul_2in_fp8(G, U, dsh))
     yq, yk, yv = fp8.qkv_fp8(dx, dsx, d["g"], sc["g"], d["u"], sc["u"], d["g"],
                              sc["g"], accum=accum)
     assert torch.equal(yq.view(torch.int16), G.view(torch.int16))
     assert torch.equal(yk.view(torch.int16), U.view(torch.int16))
     assert torch.equal(yv.view(torch.int16), G.view(torch.int16))
+
+
+@pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+@pytest.mark.parametrize("M,I,H", [(1, 16, 16), (37, 144, 64), (300, 272, 512),
+                                   (513, 1040, 1024)])
+def test_gate_up_swiglu_ragged_equals_parts(accum, M, I, H):
+    # ragged M, I not a multiple of the 128-column tile, short and long K
+    dev = device()
+    rng = np.random.default_rng(M + I + H)
+    x = workloads.activations(rng, M, H)
+    wg = workloads.weights(rng, I, H, 0.02)
+    wu = workloads.weights(rng, I, H, 0.02)
+    sx = olin.scale_from_amax(olin.amax_f32(x))
+    qx = to_dev_u8(olin.quant_static(x, sx), dev)
+    (qg, sg), (qu, su) = olin.rtn_weight(wg), olin.rtn_weight(wu)
+    dg, du = to_dev_u8(qg, dev), to_dev_u8(qu, dev)
+    dsx, dsg, dsu, dsh = (scalar(v, dev) for v in (sx, sg, su, 0.02))
+    qh = fp8.fp8_gate_up_swiglu(qx, dg, dsx, dsg, du, dsu, dsh, accum=accum)
+    G = fp8.fp8_linear(qx, dg, dsx, dsg, accum=accum)
+    U = fp8.fp8_linear(qx, du, dsx, dsu, accum=accum)
+    assert torch.equal(qh, fp8.silu_mul_2in_fp8(G, U, dsh))
