@@ -1,10 +1,10 @@
 // HBM-bound kernels of libfp8mot: static activation quantization, two-input
 // SwiGLU with FP8 output, and the amax observer.
 //
-// All three stream flat contiguous buffers: each thread handles 16 elements
-// per step (two 128-bit BF16 loads per input, one 128-bit store of 16 FP8
-// codes), the grid strides over 16-element units, and the last n % 16
-// elements are done one by one by the first threads of block 0.
+// All three stream flat contiguous buffers with 128-bit nontemporal loads and
+// stores, several in flight per thread; the grid strides over 16-element
+// units and the last n % 16 elements are done one by one by the first
+// threads of block 0.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,30 +29,44 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
 }
 
 // Static quantization: q = e4m3(x / s), one IEEE FP32 division per element.
+// A thread handles 32 elements per step (four 128-bit loads in flight, two
+// 128-bit stores), keeping enough bytes in flight to cover HBM latency.
 __global__ __launch_bounds__(kThreads) void quant_static_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int64_t n,
     const float* __restrict__ d_scale) {
   const float s = *d_scale;
-  const int64_t units = n >> 4;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t units = n >> 4;                 // 16-element units
+  const int64_t stride = (int64_t)gridDim.x * kThreads * 2;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   u32x4* qv = reinterpret_cast<u32x4*>(q);
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < units;
-       i += stride) {
-    const u32x4 a = __builtin_nontemporal_load(xv + 2 * i);
-    const u32x4 b = __builtin_nontemporal_load(xv + 2 * i + 1);
-    float f[16];
-    unpack8(a, f);
-    unpack8(b, f + 8);
-    float qf[16];
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * 2 + threadIdx.x; base < units;
+       base += stride) {
+    u32x4 a[2][2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) qf[j] = f[j] / s;   // IEEE division
-    u32x4 o;
-    o.x = e4m3_pack4(qf[0], qf[1], qf[2], qf[3]);
-    o.y = e4m3_pack4(qf[4], qf[5], qf[6], qf[7]);
-    o.z = e4m3_pack4(qf[8], qf[9], qf[10], qf[11]);
-    o.w = e4m3_pack4(qf[12], qf[13], qf[14], qf[15]);
-    __builtin_nontemporal_store(o, qv + i);
+    for (int k = 0; k < 2; ++k) {
+      const int64_t i = base + k * kThreads;
+      if (i < units) {
+        a[k][0] = __builtin_nontemporal_load(xv + 2 * i);
+        a[k][1] = __builtin_nontemporal_load(xv + 2 * i + 1);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t i = base + k * kThreads;
+      if (i < units) {
+        float f[16];
+        unpack8(a[k][0], f);
+        unpack8(a[k][1], f + 8);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) f[j] = f[j] / s;   // IEEE division
+        u32x4 o;
+        o.x = e4m3_pack4(f[0], f[1], f[2], f[3]);
+        o.y = e4m3_pack4(f[4], f[5], f[6], f[7]);
+        o.z = e4m3_pack4(f[8], f[9], f[10], f[11]);
+        o.w = e4m3_pack4(f[12], f[13], f[14], f[15]);
+        __builtin_nontemporal_store(o, qv + i);
+      }
+    }
   }
   if (blockIdx.x == 0) {
     const int64_t t = (units << 4) + threadIdx.x;
@@ -61,36 +75,50 @@ __global__ __launch_bounds__(kThreads) void quant_static_kernel(
 }
 
 // Two-input SwiGLU: q = e4m3(silu(g) * u / s_out), the division done as a
-// multiplication by the (correctly rounded) reciprocal of s_out.
+// multiplication by the (correctly rounded) reciprocal of s_out.  A thread
+// handles 32 elements per step: eight 128-bit loads in flight, two stores.
 __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ u,
     uint8_t* __restrict__ q, int64_t n, const float* __restrict__ d_s) {
   const float rs = 1.0f / *d_s;
   const int64_t units = n >> 4;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * 2;
   const u32x4* gv = reinterpret_cast<const u32x4*>(g);
   const u32x4* uv = reinterpret_cast<const u32x4*>(u);
   u32x4* qv = reinterpret_cast<u32x4*>(q);
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < units;
-       i += stride) {
-    const u32x4 g0 = __builtin_nontemporal_load(gv + 2 * i);
-    const u32x4 g1 = __builtin_nontemporal_load(gv + 2 * i + 1);
-    const u32x4 u0 = __builtin_nontemporal_load(uv + 2 * i);
-    const u32x4 u1 = __builtin_nontemporal_load(uv + 2 * i + 1);
-    float fg[16], fu[16];
-    unpack8(g0, fg);
-    unpack8(g1, fg + 8);
-    unpack8(u0, fu);
-    unpack8(u1, fu + 8);
-    float h[16];
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * 2 + threadIdx.x; base < units;
+       base += stride) {
+    u32x4 a[2][4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) h[j] = __fmul_rn(silu_mul(fg[j], fu[j]), rs);
-    u32x4 o;
-    o.x = e4m3_pack4(h[0], h[1], h[2], h[3]);
-    o.y = e4m3_pack4(h[4], h[5], h[6], h[7]);
-    o.z = e4m3_pack4(h[8], h[9], h[10], h[11]);
-    o.w = e4m3_pack4(h[12], h[13], h[14], h[15]);
-    __builtin_nontemporal_store(o, qv + i);
+    for (int k = 0; k < 2; ++k) {
+      const int64_t i = base + k * kThreads;
+      if (i < units) {
+        a[k][0] = __builtin_nontemporal_load(gv + 2 * i);
+        a[k][1] = __builtin_nontemporal_load(gv + 2 * i + 1);
+        a[k][2] = __builtin_nontemporal_load(uv + 2 * i);
+        a[k][3] = __builtin_nontemporal_load(uv + 2 * i + 1);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t i = base + k * kThreads;
+      if (i < units) {
+        float fg[16], fu[16];
+        unpack8(a[k][0], fg);
+        unpack8(a[k][1], fg + 8);
+        unpack8(a[k][2], fu);
+        unpack8(a[k][3], fu + 8);
+        float h[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) h[j] = __fmul_rn(silu_mul(fg[j], fu[j]), rs);
+        u32x4 o;
+        o.x = e4m3_pack4(h[0], h[1], h[2], h[3]);
+        o.y = e4m3_pack4(h[4], h[5], h[6], h[7]);
+        o.z = e4m3_pack4(h[8], h[9], h[10], h[11]);
+        o.w = e4m3_pack4(h[12], h[13], h[14], h[15]);
+        __builtin_nontemporal_store(o, qv + i);
+      }
+    }
   }
   if (blockIdx.x == 0) {
     const int64_t t = (units << 4) + threadIdx.x;
@@ -99,31 +127,11 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
   }
 }
 
-// Folds the finished amax into the state and clears the reduction slots.
-__device__ void observer_fold(fp8mot_observer_state_dev* st, int mode, float c) {
-  const float a = __uint_as_float(
-      __hip_atomic_load(&st->pending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  float m = st->m;
-  if (st->count == 0) {
-    m = a;
-  } else if (mode == 0) {
-    m = (a != a || m != m) ? __builtin_nanf("") : (a > m ? a : m);
-  } else {
-    const float d = __fsub_rn(a, m);
-    const float p = __fmul_rn(c, d);
-    m = __fadd_rn(m, p);
-  }
-  st->m = m;
-  st->count = st->count + 1;
-  st->pending = 0u;
-  st->arrivals = 0u;
-}
-
 // Block-wide max of non-negative FP32 bit patterns (integer order == value
 // order for non-negative floats; NaN patterns sort above +Inf) into the
-// state's pending slot; the last block to arrive folds it into the state.
-__device__ __forceinline__ void block_max_and_fold(uint32_t v, fp8mot_observer_state_dev* st,
-                                                   int mode, float c) {
+// state's pending slot.  Only a block that can raise the running value
+// issues the atomic, so the atomics do not serialize on one address.
+__device__ __forceinline__ void block_max_to(uint32_t v, uint32_t* dst) {
   __shared__ uint32_t red[kThreads / 64];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -137,36 +145,36 @@ __device__ __forceinline__ void block_max_and_fold(uint32_t v, fp8mot_observer_s
     uint32_t m = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) m = m > red[w] ? m : red[w];
-    // only blocks that can raise the running max touch the shared word, so
-    // the atomics do not serialize on one address across the whole grid
-    if (m > __hip_atomic_load(&st->pending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-      atomicMax(&st->pending, m);
-    __threadfence();
-    const uint32_t prev = atomicAdd(&st->arrivals, 1u);
-    if (prev == gridDim.x - 1) {
-      __threadfence();
-      observer_fold(st, mode, c);
-    }
+    if (m > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(dst, m);
   }
 }
 
 // amax over BF16: max of (bits & 0x7FFF) as integers is max |x| exactly.
+// Four 128-bit loads per thread per step.
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(
-    const uint16_t* __restrict__ x, int64_t n, fp8mot_observer_state_dev* st, int mode,
-    float c) {
-  const int64_t units = n >> 3;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const uint16_t* __restrict__ x, int64_t n, uint32_t* __restrict__ pending) {
+  const int64_t units = n >> 3;                 // 8-element units
+  const int64_t stride = (int64_t)gridDim.x * kThreads * 4;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < units;
-       i += stride) {
-    const u32x4 a = __builtin_nontemporal_load(xv + i);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * 4 + threadIdx.x; base < units;
+       base += stride) {
+    u32x4 a[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
-      m = m > lo ? m : lo;
-      m = m > hi ? m : hi;
+    for (int k = 0; k < 4; ++k) {
+      const int64_t i = base + k * kThreads;
+      a[k] = i < units ? __builtin_nontemporal_load(xv + i) : (u32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w[4] = {a[k].x, a[k].y, a[k].z, a[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+        m = m > lo ? m : lo;
+        m = m > hi ? m : hi;
+      }
     }
   }
   if (blockIdx.x == 0) {
@@ -176,13 +184,13 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(
       m = m > v ? m : v;
     }
   }
-  block_max_and_fold(m << 16, st, mode, c);
+  block_max_to(m << 16, pending);
 }
 
 // amax of silu(g) * u in FP32 (as silu_mul_kernel evaluates it).
 __global__ __launch_bounds__(kThreads) void amax_swiglu_kernel(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ u, int64_t n,
-    fp8mot_observer_state_dev* st, int mode, float c) {
+    uint32_t* __restrict__ pending) {
   const int64_t units = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const u32x4* gv = reinterpret_cast<const u32x4*>(g);
@@ -207,7 +215,26 @@ __global__ __launch_bounds__(kThreads) void amax_swiglu_kernel(
       m = m > v ? m : v;
     }
   }
-  block_max_and_fold(m, st, mode, c);
+  block_max_to(m, pending);
+}
+
+// Folds the pending amax into the state and clears the slot.  One thread.
+__global__ void observer_update_kernel(fp8mot_observer_state_dev* st, int mode,
+                                       float c) {
+  const float a = __uint_as_float(st->pending);
+  float m = st->m;
+  if (st->count == 0) {
+    m = a;
+  } else if (mode == 0) {
+    m = (a != a || m != m) ? __builtin_nanf("") : (a > m ? a : m);
+  } else {
+    const float d = __fsub_rn(a, m);
+    const float p = __fmul_rn(c, d);
+    m = __fadd_rn(m, p);
+  }
+  st->m = m;
+  st->count = st->count + 1;
+  st->pending = 0u;
 }
 
 __global__ void scale_from_state_kernel(const fp8mot_observer_state_dev* st,
@@ -227,7 +254,7 @@ int grid_for(int64_t units, int max_blocks) {
 hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                                const float* d_scale, int max_blocks,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(n >> 4, max_blocks)),
+  hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(n >> 5, max_blocks)),
                      dim3(kThreads), 0, stream, x, q, n, d_scale);
   return hipGetLastError();
 }
@@ -235,7 +262,7 @@ hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
 hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
                            int64_t n, const float* d_s, int max_blocks,
                            hipStream_t stream) {
-  hipLaunchKernelGGL(silu_mul_kernel, dim3(grid_for(n >> 4, max_blocks)),
+  hipLaunchKernelGGL(silu_mul_kernel, dim3(grid_for(n >> 5, max_blocks)),
                      dim3(kThreads), 0, stream, g, u, q, n, d_s);
   return hipGetLastError();
 }
@@ -243,15 +270,17 @@ hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
 hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,
                           fp8mot_observer_state_dev* st, int mode, float c,
                           int max_blocks, hipStream_t stream) {
-  // a reduction needs few blocks: two per CU, each striding over the input
-  max_blocks = max_blocks / 4 > 0 ? max_blocks / 4 : 1;
+  // read-only: twice the workgroups of the read-write kernels
   if (u == nullptr) {
-    hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid_for(n >> 3, max_blocks)),
-                       dim3(kThreads), 0, stream, x, n, st, mode, c);
+    hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid_for(n >> 5, 2 * max_blocks)),
+                       dim3(kThreads), 0, stream, x, n, &st->pending);
   } else {
     hipLaunchKernelGGL(amax_swiglu_kernel, dim3(grid_for(n >> 3, max_blocks)),
-                       dim3(kThreads), 0, stream, x, u, n, st, mode, c);
+                       dim3(kThreads), 0, stream, x, u, n, &st->pending);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(observer_update_kernel, dim3(1), dim3(1), 0, stream, st, mode, c);
   return hipGetLastError();
 }
 
