@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="rows of X in the oracle's timed sample")
+    p.add_argument("--no-large", action="store_true",
+                   help="skip the large-MLP-size elementwise measurement")
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="also run one plain device copy of this many MiB (a "
                         "known-size reference for the profiler's byte counters)")
@@ -208,9 +210,55 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
         "fp8_mfma_engine": fp8_engine,
+        "elementwise_large": large,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out))
+
+
+def elementwise_large(fp8, torch, dev, stream):
+    """The HBM-bound kernels at the large gated-MLP sizes (X [16384, 5120],
+    G/U [16384, 25600]), where the working sets exceed the 256 MB MALL:
+    average launch time over back-to-back launches (three rotating X copies
+    for quantize), algorithmic GB/s, and the fraction of the 8 TB/s peak.
+    A plain device copy of the SwiGLU's byte count is timed beside them."""
+    def timed(f, reps):
+        for r in range(2):
+            f(r)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            f(r)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {}
+    n = 16384 * 5120
+    xs = [torch.randn(n, device=dev).to(torch.bfloat16) for _ in range(3)]
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    s = torch.tensor([0.02], device=dev)
+    us = timed(lambda r: fp8.fp8_quant_static(xs[r % 3], s, out=q), 20)
+    out["quant_16384x5120"] = {"us": us, "bytes": 3 * n, "GB/s": 3 * n / us / 1e3,
+                               "frac_hbm": 3 * n / us / 1e3 / HBM_PEAK_GBS}
+    del xs, q
+    n = 16384 * 25600
+    g = torch.randn(n, device=dev).to(torch.bfloat16)
+    u = torch.randn(n, device=dev).to(torch.bfloat16)
+    q = torch.empty(n, dtype=torch.uint8, device=dev)
+    us = timed(lambda r: fp8.silu_mul_2in_fp8(g, u, s, out=q), 8)
+    out["silu_16384x25600"] = {"us": us, "bytes": 5 * n, "GB/s": 5 * n / us / 1e3,
+                               "frac_hbm": 5 * n / us / 1e3 / HBM_PEAK_GBS}
+    del q
+    a = g.view(torch.uint8)
+    b = torch.empty_like(a)
+    us = timed(lambda r: b.copy_(a), 8)
+    out["device_copy_same_bytes"] = {"us": us, "GB/s": 2 * a.numel() / us / 1e3}
+    del g, u, a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def recorded_traffic(key):

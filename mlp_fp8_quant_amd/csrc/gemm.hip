@@ -9,15 +9,11 @@
 //
 // Two accumulation engines share the tiling:
 //
-//  ENGINE_F16 (FP8MOT_ACC_EXACT): the FP8 codes are decoded exactly to F16 on
-//    their way from global memory into LDS and multiplied with
-//    v_mfma_f32_32x32x16_f16.  Every E4M3 value, subnormals included, is an
-//    F16 value after scaling by 2^-8: ((code << 8) as int16 >> 1) with bit 14
-//    cleared puts the sign at bit 15, the 4 exponent bits at 13..10 and the 3
-//    mantissa bits at 9..7, i.e. the F16 with the same fields under bias 15
-//    instead of 7 -- value * 2^-8 for normals and subnormals alike.  The
-//    epilogue multiplies by 2^16 (exact).  This engine's products are summed
-//    to FP32 precision.
+//  ENGINE_F16 (FP8MOT_ACC_EXACT): the FP8 codes are staged through LDS as
+//    bytes and decoded exactly to F16 right after each fragment read (the
+//    gfx950 packed FP8 -> F16 conversion at scale 1.0: every E4M3 value is an
+//    F16 value, NaN stays NaN), then multiplied with v_mfma_f32_32x32x16_f16,
+//    whose products are summed to FP32 precision.
 //
 //  ENGINE_FP8 (FP8MOT_ACC_FP8_MFMA): the codes go to LDS as bytes and are
 //    multiplied with v_mfma_f32_32x32x64_f8f6f4 at twice the rate.  On gfx950
@@ -63,7 +59,6 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef short v2s __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -89,13 +84,13 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n,
   tn = in_band / rows;
 }
 
-// Two E4M3 codes (bytes b0, b1 of x selected by `sel`) -> two F16 bit
-// patterns (value * 2^-8) packed in one dword.
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t x, uint32_t sel) {
-  const uint32_t t = __builtin_amdgcn_perm(0u, x, sel);  // codes in bytes 1, 3
-  v2s h = __builtin_bit_cast(v2s, t);
-  h = h >> (v2s){1, 1};                                  // arithmetic, per half
-  return __builtin_bit_cast(uint32_t, h) & 0xBFFFBFFFu;
+// Two E4M3 codes (the low or high half of a dword) -> two F16 values with the gfx950
+// packed conversion at scale 1.0.  Every finite E4M3 value is exactly an F16
+// value (max 448, smallest subnormal 2^-9 is an F16 normal) and the NaN codes
+// become an F16 NaN; all 256 codes were checked on the hardware.
+template <bool HIGH>
+__device__ __forceinline__ int e4m3x2_to_f16x2(uint32_t x) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, HIGH));
 }
 
 // Buffer resource over [base, base + bytes): loads beyond it return 0 and
@@ -113,9 +108,8 @@ constexpr int kOOB = 0x7FFFFFF0;  // a byte offset past every buffer
 
 // ENGINE: 0 = F16 (exact decode), 1 = native FP8 MFMA.
 //
-// Pipeline: a stage covers KS = 64 (F16 engine) or 128 (FP8 engine) of K;
-// its LDS rows are 128 bytes either way (64 F16 or 128 codes).  LDS holds two
-// stages.  While stage s is multiplied out of one LDS buffer, the registers
+// Pipeline: a stage covers 128 of K; its LDS rows are the 128 FP8 codes of a
+// row (both engines keep codes in LDS).  LDS holds two stages.  While stage s is multiplied out of one LDS buffer, the registers
 // hold stage s+1 (loaded during stage s-1); half-way through stage s's
 // MFMAs they are written to the other buffer and the loads of stage s+2 are
 // issued into the freed registers.  A load therefore has a whole stage of
@@ -145,7 +139,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   constexpr int T = WM * WN * 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
-  constexpr int KS = ENGINE == 0 ? 64 : 128;    // K per stage
+  constexpr int KS = 128;                       // K per stage
   constexpr int GCH = KS / 16;                  // 16-byte global chunks per row
   constexpr int A_LD = BM * GCH / T, B_LD = BN * GCH / T;
   static_assert(A_LD * T == BM * GCH && B_LD * T == BN * GCH, "tile/threads");
@@ -210,23 +204,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   // one 16-byte global chunk (row r, chunk c) into LDS
   auto put = [&](uint8_t* base, int r, int c, v4i v) {
     uint8_t* row = base + r * kRowBytes;
-    const int sw = (r >> 1) & 7;
-    if constexpr (ENGINE == 0) {
-      // 16 codes -> 16 F16 = LDS chunks 2c and 2c + 1
-      v4i lo, hi;
-      lo[0] = e4m3x2_to_f16x2(v[0], 0x010C000Cu);
-      lo[1] = e4m3x2_to_f16x2(v[0], 0x030C020Cu);
-      lo[2] = e4m3x2_to_f16x2(v[1], 0x010C000Cu);
-      lo[3] = e4m3x2_to_f16x2(v[1], 0x030C020Cu);
-      hi[0] = e4m3x2_to_f16x2(v[2], 0x010C000Cu);
-      hi[1] = e4m3x2_to_f16x2(v[2], 0x030C020Cu);
-      hi[2] = e4m3x2_to_f16x2(v[3], 0x010C000Cu);
-      hi[3] = e4m3x2_to_f16x2(v[3], 0x030C020Cu);
-      *reinterpret_cast<v4i*>(row + (((2 * c) ^ sw) << 4)) = lo;
-      *reinterpret_cast<v4i*>(row + (((2 * c + 1) ^ sw) << 4)) = hi;
-    } else {
-      *reinterpret_cast<v4i*>(row + ((c ^ sw) << 4)) = v;
-    }
+    *reinterpret_cast<v4i*>(row + ((c ^ ((r >> 1) & 7)) << 4)) = v;
   };
   auto sstore = [&](int buf) {
     uint8_t* sa = smem + buf * STAGE;
@@ -254,22 +232,25 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   auto chunk = [&](const uint8_t* base, int r, int c) -> v4i {
     return *reinterpret_cast<const v4i*>(base + r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4));
   };
-  constexpr int NSTEP = ENGINE == 0 ? 4 : 2;   // MFMA K-steps per stage
-  // operand fragments, double-buffered: K-step s of a stage uses slot s & 1
+  // Fragment steps per stage.  FP8 engine: two K-steps of 64, a lane reading
+  // two chunks (32 codes) per operand.  F16 engine: four steps of 32 K, a
+  // lane reading one chunk (16 codes) per operand, converting it to two F16
+  // operands and issuing two 32x32x16 MFMAs -- bytes 0..7 of every lane's
+  // chunk feed the first, bytes 8..15 the second, for A and B alike.
+  constexpr int NSTEP = ENGINE == 0 ? 4 : 2;
+  // operand fragments (raw codes), double-buffered: step s uses slot s & 1
   // (NSTEP is even, so the slot of step s is the same in every stage)
-  typedef typename std::conditional<ENGINE == 0, f16x8, v8i>::type frag_t;
+  typedef typename std::conditional<ENGINE == 0, v4i, v8i>::type frag_t;
   frag_t fa[2][FM], fb[2][FN];
-  auto rd = [&](int buf, int s, int slot) {   // fragments of K-step s
+  auto rd = [&](int buf, int s, int slot) {   // fragments of step s
     const uint8_t* sa = smem + buf * STAGE;
     const uint8_t* sb = sa + BM * kRowBytes;
     if constexpr (ENGINE == 0) {
       const int c = 2 * s + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[slot][i] = __builtin_bit_cast(f16x8, chunk(sa, wm * WTM + i * 32 + (lane & 31), c));
+      for (int i = 0; i < FM; ++i) fa[slot][i] = chunk(sa, wm * WTM + i * 32 + (lane & 31), c);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        fb[slot][j] = __builtin_bit_cast(f16x8, chunk(sb, wn * WTN + j * 32 + (lane & 31), c));
+      for (int j = 0; j < FN; ++j) fb[slot][j] = chunk(sb, wn * WTN + j * 32 + (lane & 31), c);
     } else {
       const int c = 4 * s + 2 * (lane >> 5);
 #pragma unroll
@@ -285,16 +266,39 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
     }
   };
   auto mf = [&](int slot) {
+    if constexpr (ENGINE == 0) {
+      f16x8 a0[FM], a1[FM], b0[FN], b1[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        const v4i v = fa[slot][i];
+        a0[i] = __builtin_bit_cast(f16x8, (v4i){e4m3x2_to_f16x2<false>(v[0]), e4m3x2_to_f16x2<true>(v[0]),
+                                                e4m3x2_to_f16x2<false>(v[1]), e4m3x2_to_f16x2<true>(v[1])});
+        a1[i] = __builtin_bit_cast(f16x8, (v4i){e4m3x2_to_f16x2<false>(v[2]), e4m3x2_to_f16x2<true>(v[2]),
+                                                e4m3x2_to_f16x2<false>(v[3]), e4m3x2_to_f16x2<true>(v[3])});
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        if constexpr (ENGINE == 0)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0);
-        else
+        const v4i v = fb[slot][j];
+        b0[j] = __builtin_bit_cast(f16x8, (v4i){e4m3x2_to_f16x2<false>(v[0]), e4m3x2_to_f16x2<true>(v[0]),
+                                                e4m3x2_to_f16x2<false>(v[1]), e4m3x2_to_f16x2<true>(v[1])});
+        b1[j] = __builtin_bit_cast(f16x8, (v4i){e4m3x2_to_f16x2<false>(v[2]), e4m3x2_to_f16x2<true>(v[2]),
+                                                e4m3x2_to_f16x2<false>(v[3]), e4m3x2_to_f16x2<true>(v[3])});
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0, 0, 0, 0);
-      }
+    }
   };
 
   // Software pipeline, per stage kt (LDS buffer kt & 1):
@@ -358,9 +362,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   }
   __syncthreads();
 
-  // ---- epilogue: y = fp32(acc [* 2^16]) * alpha, then the output format ----
-  // F16 engine: both operands carried a 2^-8 factor
-  const float undo = ENGINE == 0 ? 65536.0f : 1.0f;
+  // ---- epilogue: y = fp32(acc * alpha), then the output format ----
   const float alpha = __fmul_rn(*g.sx, *g.sw);
   void* __restrict__ C = g.C;
   constexpr int ESZ = OUT == 0 ? 2 : (OUT == 1 ? 1 : 4);
@@ -387,8 +389,8 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
         for (int v = 0; v < 16; ++v) {
           const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
           const int c = p * 32 + (lane & 31);
-          const float yg = __fmul_rn(__fmul_rn(acc[i][2 * p][v], undo), alpha);
-          const float yu = __fmul_rn(__fmul_rn(acc[i][2 * p + 1][v], undo), alpha_u);
+          const float yg = __fmul_rn(acc[i][2 * p][v], alpha);
+          const float yu = __fmul_rn(acc[i][2 * p + 1][v], alpha_u);
           const float h = silu_mul(bf16_to_f32(f32_to_bf16(yg)), bf16_to_f32(f32_to_bf16(yu)));
           wbuf[r * LROW + c] = (uint8_t)e4m3_encode(__fmul_rn(h, rs));
         }
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
           for (int v = 0; v < 16; ++v) {
             const int r = ii * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
             const int c = j * 32 + (lane & 31);
-            const float y = __fmul_rn(__fmul_rn(acc[h * HALF + ii][j][v], undo), alpha);
+            const float y = __fmul_rn(acc[h * HALF + ii][j][v], alpha);
             *reinterpret_cast<uint16_t*>(wbuf + r * LROW + c * 2) = (uint16_t)f32_to_bf16(y);
           }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
           const int row = row_l + i * 32 + (v >> 2) * 8 + (v & 3);
           const bool ok = (m0 + row < M) && (n0 + col < N);
           const int off = ok ? (row * N + n0 + col) * ESZ : kOOB;
-          const float y = __fmul_rn(__fmul_rn(acc[i][j][v], undo), alpha);
+          const float y = __fmul_rn(acc[i][j][v], alpha);
           if constexpr (OUT == 1)
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e4m3_encode(y / sy), rc_rs, off, 0, 0);
           else
