@@ -197,6 +197,16 @@ def main():
                      "unit": "TFLOP/s", "frac": f8 / FP8_PEAK_TFLOPS},
     }
 
+    large = None if args.no_large else elementwise_large(fp8, torch, dev, stream)
+
+    if args.copy_calib_mb > 0:
+        n = args.copy_calib_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_rows)
