@@ -25,16 +25,14 @@
 // Tiling (both engines):
 //  * a workgroup computes a BM x BN tile with WM x WN waves, each wave a
 //    (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks;
-//  * operands are K-contiguous ([M,K] and [N,K]); per stage, a slab of 128
-//    LDS bytes per row (64 K for F16, 128 K for FP8) of A and B is staged,
-//    double buffered: the global loads of stage s+1 are issued before the
-//    MFMAs of stage s and written to the other buffer after them, one barrier
-//    per stage;
-//  * the 16-byte chunk c of LDS row r lives at chunk c ^ ((r >> 1) & 7): the
+//  * operands are K-contiguous ([M,K] and [N,K]); a stage holds 64 K of the
+//    tile's A and B rows (64 LDS bytes per row), four stages live in LDS and
+//    the buffer unit copies them from memory straight into LDS, three stages
+//    ahead of the MFMAs, one barrier per stage (details below);
+//  * the 16-byte chunk c of LDS row r lives at chunk c ^ ((r >> 2) & 3): the
 //    LDS serves a 128-bit access 16 lanes at a time across 64 four-byte
-//    banks (256 bytes), and 16 consecutive rows of one logical chunk then
-//    cover all 16 distinct 16-byte bank groups (two rows share each 256-byte
-//    bank window, and their swizzled chunks differ);
+//    banks (256 bytes = four rows), and 16 consecutive rows of one logical
+//    chunk then cover all 16 distinct 16-byte bank groups;
 //  * an MFMA operand fragment is read per lane as whole 16-byte chunks: lane
 //    l takes row l % 32 and K positions (l / 32) * w .. + w of the MFMA's K
 //    step (w = 8 for F16, 32 for FP8); A and B use the same assignment, so the
@@ -43,7 +41,16 @@
 //    column l % 32 of its 32x32 block;
 //  * tiles are ordered so that the workgroups dealt to one XCD (blocks go to
 //    the 8 XCDs round-robin) walk a band of neighbouring tiles and share A and
-//    B rows in that XCD's L2.
+//    B rows in that XCD's L2;
+//  * the epilogue scales the accumulators, converts them (BF16, or SwiGLU to
+//    FP8 in the fused gate/up kernel), transposes 4x4 blocks inside lane
+//    quads so each lane owns consecutive columns of one row, and stores them
+//    straight to memory.
+//
+// On MI355X the matrix cores slow down with the data they multiply (random
+// codes draw more power than zeros, and the clock drops), so kernel times
+// depend on the operands; the kernels keep every instruction that is not an
+// MFMA to a minimum.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -62,7 +69,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kRowBytes = 128;  // LDS bytes per row per stage
 constexpr int kNumXcd = 8;      // MI355X: 8 XCDs
 constexpr int kGroupM = 8;      // tile rows per band
 
@@ -106,15 +112,101 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
 
 constexpr int kOOB = 0x7FFFFFF0;  // a byte offset past every buffer
 
-// ENGINE: 0 = F16 (exact decode), 1 = native FP8 MFMA.
-//
-// Pipeline: a stage covers 128 of K; its LDS rows are the 128 FP8 codes of a
-// row (both engines keep codes in LDS).  LDS holds two stages.  While stage s is multiplied out of one LDS buffer, the registers
-// hold stage s+1 (loaded during stage s-1); half-way through stage s's
-// MFMAs they are written to the other buffer and the loads of stage s+2 are
-// issued into the freed registers.  A load therefore has a whole stage of
-// MFMA work to arrive, and the LDS writes run while the first half's MFMAs
-// are still in the matrix pipe.  One barrier per stage.
+// The same raw-buffer descriptor as four dwords (base address, stride 0,
+// size in bytes, the configuration dword) for the inline-assembly copy below.
+__device__ __forceinline__ v4i make_rsrc_words(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0 : (int)bytes;
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (v4i){(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFF), n, 0x00020000};
+}
+
+// One wave-wide 16-byte-per-lane copy from a buffer straight into LDS
+// (buffer_load_dwordx4 ... lds): lane i's bytes land at lds_addr + 16 * i,
+// out-of-range lanes write zeros.  Written as assembly so that the compiler,
+// which cannot tell which stage buffer a copy writes, does not make every
+// LDS read wait for every copy; the kernel waits for its copies itself
+// (s_waitcnt vmcnt) before the barrier that publishes a stage.  M0 holds the
+// LDS address; one wait state separates its write from the copy.
+__device__ __forceinline__ void copy_to_lds(v4i rsrc, uint32_t lds_addr, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> two BF16 (round to nearest even) packed lo | hi << 16,
+// with the gfx950 packed conversion.  For every non-NaN input it gives the
+// bits of the integer rounding in device_common.h (checked on the hardware
+// over all 2^32 patterns); a NaN stays a NaN.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// Lane t of a quad holds byte e = row e of column t; afterwards it holds
+// byte e = column e of row t (a 4x4 byte transpose across the quad).
+__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t x, int t) {
+  // exchange 16-bit halves with lane t ^ 2, then bytes with lane t ^ 1
+  const uint32_t p = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  const uint32_t z = __builtin_amdgcn_perm(p, x, t < 2 ? 0x05040100u : 0x03020706u);
+  const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)z, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  return __builtin_amdgcn_perm(r, z, (t & 1) ? 0x03070105u : 0x06020400u);
+}
+
+// Lane t of a quad holds four 16-bit values of column t, rows 0..3, as
+// a = row0 | row1 << 16 and b = row2 | row3 << 16; afterwards d0, d1 hold
+// row t, columns 0..3 (d0 = col0 | col1 << 16, d1 = col2 | col3 << 16).
+__device__ __forceinline__ void quad_transpose_halves(uint32_t a, uint32_t b, int t,
+                                                      uint32_t& d0, uint32_t& d1) {
+  // lanes 0, 1 keep rows 0-1 and take those of columns t + 2; lanes 2, 3
+  // keep rows 2-3 and take those of columns t - 2
+  const uint32_t send = t < 2 ? b : a;
+  const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, true);
+  const uint32_t u = t < 2 ? a : got;    // rows ra, ra+1 of column t & 1
+  const uint32_t v = t < 2 ? got : b;    // rows ra, ra+1 of column (t & 1) + 2
+  // even lanes keep row ra and send row ra+1; odd lanes the reverse
+  const uint32_t s2 = (t & 1) ? __builtin_amdgcn_perm(v, u, 0x05040100u)    // u.lo | v.lo << 16
+                              : __builtin_amdgcn_perm(v, u, 0x07060302u);   // u.hi | v.hi << 16
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s2, 0xB1, 0xF, 0xF, true);
+  if (t & 1) {
+    d0 = __builtin_amdgcn_perm(u, r2, 0x07060100u);   // r2.lo | u.hi << 16
+    d1 = __builtin_amdgcn_perm(v, r2, 0x07060302u);   // r2.hi | v.hi << 16
+  } else {
+    d0 = __builtin_amdgcn_perm(r2, u, 0x05040100u);   // u.lo | r2.lo << 16
+    d1 = __builtin_amdgcn_perm(r2, v, 0x07060100u);   // v.lo | r2.hi << 16
+  }
+}
+
+// Operand staging: a stage covers KS = 64 of K.  Its LDS rows hold the 64
+// FP8 codes of one A or B row (A rows first, then B rows), and NB = 4 stages
+// live in LDS at once.  The global -> LDS copy is done by the buffer unit
+// itself (buffer_load_dwordx4 with the LDS flag): one wave-wide instruction
+// fills 1 KB of a stage -- lane i's 16 bytes land at byte 16*i -- with no
+// registers in between and no wait in the wave.  Loads that fall outside a
+// buffer resource write zeros, which pads ragged M, N and K.  The copies of
+// stage s + NB go out as soon as every wave has finished reading stage s,
+// spread between the MFMAs of that step, so three stages are always in
+// flight.  (Measured on MI355X: staging through registers and ds_write, or
+// 3 or 5 stages, is no faster.)
+constexpr int KS = 64;            // K per stage
+constexpr int NB = 4;             // stages resident in LDS
+constexpr int CH = KS / 16;       // 16-byte chunks per LDS row
+constexpr int RW = 256 / KS;      // LDS rows per 256-byte bank window
+constexpr int RPI = 1024 / KS;    // LDS rows filled by one wave-wide copy
+
+// Physical chunk of logical chunk c in LDS row r.  The LDS serves a 128-bit
+// access 16 lanes at a time across 64 four-byte banks (256 bytes = RW rows);
+// the 16 lanes of a fragment read touch 16 consecutive rows at one logical
+// chunk, and the XOR with the row's window index spreads them over all 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r / RW) & (CH - 1)); }
+
 struct GemmArgs {
   const uint8_t* A;   // [M, K]
   const uint8_t* B;   // [N, K]   (fused: the gate weight)
@@ -128,97 +220,72 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 // OUT: 0 BF16, 1 FP8, 2 FP32.  FUSED: gate and up GEMMs of a gated MLP in one
 // tile (BN = 256 = 128 gate rows + 128 up rows of the same output columns)
 // whose epilogue applies SwiGLU and writes FP8, bit for bit what the separate
 // BF16 GEMMs followed by silu_mul_2in_fp8 produce.
-template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED, int PIPE>
+template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
-  const uint8_t* __restrict__ A = g.A;
   const int M = g.M, N = g.N, K = g.K;
-  constexpr int T = WM * WN * 64;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
-  constexpr int KS = 128;                       // K per stage
-  constexpr int GCH = KS / 16;                  // 16-byte global chunks per row
-  constexpr int A_LD = BM * GCH / T, B_LD = BN * GCH / T;
-  static_assert(A_LD * T == BM * GCH && B_LD * T == BN * GCH, "tile/threads");
-  constexpr int STAGE = (BM + BN) * kRowBytes;
+  constexpr int STAGE = (BM + BN) * KS;
+  constexpr int A_INS = BM / RPI, INS = (BM + BN) / RPI;   // wave-wide copies per stage
+  constexpr int LPW = INS / NW;                            // ... per wave
+  static_assert(LPW * NW == INS, "tile rows / waves");
   static_assert(!FUSED || (BN == 256 && FN % 2 == 0), "fused tiles pair gate/up blocks");
-  constexpr int EPI = FUSED ? WM * WN * WTM * (WTN / 2 + 16)
-                            : WM * WN * (FM / 2 > 0 ? FM / 2 : 1) * 32 * (WTN * 2 + 16);
-  constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  static_assert(NB * STAGE <= 160 * 1024, "stages fit the 160 KB LDS of a CU");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
+  auto stage_buf = [&](int b) -> uint8_t* { return smem + b * STAGE; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   // output columns of this tile start at n0 (fused: 128 of each of G and U)
   const int m0 = tm * BM, n0 = tn * (FUSED ? BN / 2 : BN);
 
-  // operand windows start at the tile's first row; rows past M read as 0
-  const __amdgpu_buffer_rsrc_t ra_rs = make_rsrc(A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
-  const __amdgpu_buffer_rsrc_t rb_rs = make_rsrc(g.B + (int64_t)n0 * K, (int64_t)(N - n0) * K);
-  const __amdgpu_buffer_rsrc_t rb2_rs =
-      FUSED ? make_rsrc(g.B2 + (int64_t)n0 * K, (int64_t)(N - n0) * K) : rb_rs;
-  // per-thread byte offsets of its chunks at K = 0 (or past the buffer).
-  // Fused: load rows 0..127 are gate rows, 128..255 the up rows of the same
-  // output columns (chunk index i < B_LD / 2 is gate, the rest up).
-  int a_off[A_LD], b_off[B_LD];
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int id = tid + i * T, r = id / GCH;
-    a_off[i] = (m0 + r < M) ? r * K + (id % GCH) * 16 : kOOB;
-  }
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int id = tid + i * T, r = (id / GCH) % (FUSED ? BN / 2 : BN);
-    b_off[i] = (n0 + r < N) ? r * K + (id % GCH) * 16 : kOOB;
-  }
-  const int my_kc = (tid % GCH) * 16;   // the chunk's K offset inside a stage
+  // operand windows start at the tile's first row; rows past M (N) read as 0
+  const v4i ra_rs = make_rsrc_words(g.A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
+  const v4i rb_rs = make_rsrc_words(g.B + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+  const v4i rb2_rs = FUSED ? make_rsrc_words(g.B2 + (int64_t)n0 * K, (int64_t)(N - n0) * K) : rb_rs;
 
-  v4i ra[A_LD], rb[B_LD];
-  auto gload = [&](int k0) {
-    const bool kin = k0 + my_kc < K;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i)
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          ra_rs, (kin && a_off[i] != kOOB) ? a_off[i] + k0 : kOOB, 0, 0);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          (FUSED && i >= B_LD / 2) ? rb2_rs : rb_rs,
-          (kin && b_off[i] != kOOB) ? b_off[i] + k0 : kOOB, 0, 0);
-  };
-  // LDS row of B load row r.  Fused: 32-row blocks alternate gate / up, so a
+  // Copy q (= wave * LPW + i) of a stage fills LDS rows q*RPI .. q*RPI+RPI-1
+  // (A rows, then B rows); lane l brings row q*RPI + l/CH, physical chunk
+  // l % CH, i.e. logical chunk swz(row, l % CH) of the row's 64 K.  Fused:
+  // B's LDS rows come in 32-row blocks alternating gate / up, so that a
   // wave's 32x32 blocks j (gate) and j + 1 (up) cover the same columns.
-  auto b_row = [&](int r) -> int {
-    if constexpr (FUSED) {
-      const int q = r & 127;
-      return 64 * (q >> 5) + (r >= 128 ? 32 : 0) + (q & 31);
+  int goff[LPW], gkc[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int q = wave * LPW + i;
+    const int lr = (q < A_INS ? q : q - A_INS) * RPI + lane / CH;   // row in the A or B region
+    const int c = swz(lr, lane % CH);
+    int grow, lim;
+    if (q < A_INS) {
+      grow = lr;
+      lim = M - m0;
     } else {
-      return r;
+      grow = FUSED ? (lr >> 6) * 32 + (lr & 31) : lr;
+      lim = N - n0;
     }
+    goff[i] = grow < lim ? grow * K + c * 16 : kOOB;
+    gkc[i] = c * 16;
+  }
+  auto issue_copy = [&](int b, int s, int i) {   // copy i of this wave for stage s into buffer b
+    const int k0 = s * KS;
+    const int q = wave * LPW + i;
+    const v4i rs = q < A_INS ? ra_rs : ((FUSED && (((q - A_INS) * RPI) & 32)) ? rb2_rs : rb_rs);
+    const int off = (goff[i] != kOOB && k0 + gkc[i] < K) ? goff[i] + k0 : kOOB;
+    copy_to_lds(rs, (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)(stage_buf(b) + q * 1024)), off);
   };
-  // one 16-byte global chunk (row r, chunk c) into LDS
-  auto put = [&](uint8_t* base, int r, int c, v4i v) {
-    uint8_t* row = base + r * kRowBytes;
-    *reinterpret_cast<v4i*>(row + ((c ^ ((r >> 1) & 7)) << 4)) = v;
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* sa = smem + buf * STAGE;
-    uint8_t* sb = sa + BM * kRowBytes;
+  auto issue_stage = [&](int b, int s) {
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int id = tid + i * T;
-      put(sa, id / GCH, id % GCH, ra[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int id = tid + i * T;
-      put(sb, b_row(id / GCH), id % GCH, rb[i]);
-    }
+    for (int i = 0; i < LPW; ++i) issue_copy(b, s, i);
   };
 
   v16f acc[FM][FN];
@@ -230,29 +297,29 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   auto chunk = [&](const uint8_t* base, int r, int c) -> v4i {
-    return *reinterpret_cast<const v4i*>(base + r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4));
+    return *reinterpret_cast<const v4i*>(base + r * KS + (swz(r, c) << 4));
   };
-  // Fragment steps per stage.  FP8 engine: two K-steps of 64, a lane reading
-  // two chunks (32 codes) per operand.  F16 engine: four steps of 32 K, a
-  // lane reading one chunk (16 codes) per operand, converting it to two F16
+  // K-steps per stage.  FP8 engine: one step of 64 K, a lane reading two
+  // chunks (32 codes) per operand.  F16 engine: two steps of 32 K, a lane
+  // reading one chunk (16 codes) per operand, converting it to two F16
   // operands and issuing two 32x32x16 MFMAs -- bytes 0..7 of every lane's
   // chunk feed the first, bytes 8..15 the second, for A and B alike.
-  constexpr int NSTEP = ENGINE == 0 ? 4 : 2;
-  // operand fragments (raw codes), double-buffered: step s uses slot s & 1
-  // (NSTEP is even, so the slot of step s is the same in every stage)
+  constexpr int NSTEP = ENGINE == 0 ? KS / 32 : KS / 64;
+  // operand fragments (raw codes), double-buffered: K-step t of the whole
+  // loop uses slot t & 1
   typedef typename std::conditional<ENGINE == 0, v4i, v8i>::type frag_t;
   frag_t fa[2][FM], fb[2][FN];
-  auto rd = [&](int buf, int s, int slot) {   // fragments of step s
-    const uint8_t* sa = smem + buf * STAGE;
-    const uint8_t* sb = sa + BM * kRowBytes;
+  auto rd = [&](int b, int st, int slot) {   // fragments of step st of the stage in buffer b
+    const uint8_t* sa = stage_buf(b);
+    const uint8_t* sb = sa + BM * KS;
     if constexpr (ENGINE == 0) {
-      const int c = 2 * s + (lane >> 5);
+      const int c = 2 * st + (lane >> 5);
 #pragma unroll
       for (int i = 0; i < FM; ++i) fa[slot][i] = chunk(sa, wm * WTM + i * 32 + (lane & 31), c);
 #pragma unroll
       for (int j = 0; j < FN; ++j) fb[slot][j] = chunk(sb, wn * WTN + j * 32 + (lane & 31), c);
     } else {
-      const int c = 4 * s + 2 * (lane >> 5);
+      const int c = 4 * st + 2 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * WTM + i * 32 + (lane & 31);
@@ -264,8 +331,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
         fb[slot][j] = __builtin_shufflevector(chunk(sb, r, c), chunk(sb, r, c + 1), 0, 1, 2, 3, 4, 5, 6, 7);
       }
     }
+    // keep the reads ahead of the MFMAs that follow, so that their latency
+    // is covered by this step's matrix work
+    __builtin_amdgcn_sched_barrier(0);
   };
-  auto mf = [&](int slot) {
+  // MFMAs of one K-step.  With copies, the copies of stage cs into buffer cb
+  // are issued one after each 32-row block of A (the rest after the last),
+  // so that the address unit is fed steadily instead of every wave queueing
+  // its copies at once.
+  auto mf = [&](int slot, auto copies, int cb, int cs) {
+    constexpr bool kCopies = decltype(copies)::value;
     if constexpr (ENGINE == 0) {
       f16x8 a0[FM], a1[FM], b0[FN], b1[FN];
 #pragma unroll
@@ -285,84 +360,101 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
                                                 e4m3x2_to_f16x2<false>(v[3]), e4m3x2_to_f16x2<true>(v[3])});
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[i], b0[j], acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[i], b1[j], acc[i][j], 0, 0, 0);
         }
+        if constexpr (kCopies) { if (i < LPW) issue_copy(cb, cs, i); }
+      }
     } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        if constexpr (kCopies) { if (i < LPW) issue_copy(cb, cs, i); }
+      }
+    }
+    if constexpr (kCopies) {
+#pragma unroll
+      for (int r = FM; r < LPW; ++r) issue_copy(cb, cs, r);
     }
   };
+  // wait until at most n of this wave's stage copies are still in flight
+  // (s_waitcnt vmcnt(n), expcnt and lgkmcnt left alone: gfx9 encoding)
+  auto wait_copies = [&](int n) {
+    if (NB > 4 && n >= 4 * LPW) __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * LPW) & 15) | (((4 * LPW) >> 4) << 14));
+    else if (NB > 3 && n >= 3 * LPW) __builtin_amdgcn_s_waitcnt(0x0F70 | ((3 * LPW) & 15) | (((3 * LPW) >> 4) << 14));
+    else if (NB > 2 && n >= 2 * LPW) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * LPW) & 15) | (((2 * LPW) >> 4) << 14));
+    else if (n >= LPW) __builtin_amdgcn_s_waitcnt(0x0F70 | (LPW & 15) | ((LPW >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+  static_assert(NB >= 2 && NB <= 5 && (NB - 1) * LPW < 64, "wait_copies covers up to four stages in flight");
 
-  // Software pipeline, per stage kt (LDS buffer kt & 1):
-  //  step 0:        issue the fragment reads of step 1, write stage kt+1 from
-  //                 the registers into the other LDS buffer and refill the
-  //                 registers with the loads of stage kt+2, then the MFMAs of
-  //                 step 0 (their fragments were read one step earlier);
-  //  steps 1..n-2:  fragment reads of the next step, MFMAs of this step;
-  //  step n-1:      barrier (every wave has written stage kt+1 and read all
-  //                 of stage kt), fragment reads of stage kt+1 step 0 from the
-  //                 other buffer, MFMAs of step n-1.
+  // Pipeline, per stage s (buffer s % NB), K-steps t = 0 .. NSTEP-1:
+  //  * before the MFMAs of step t, the fragments of the next step are read
+  //    into the other register slot;
+  //  * at the last step, the next stage must be ready: wait for this wave's
+  //    copies of stage s + 1 and for its own fragment reads of stage s,
+  //    barrier (every wave's copies of s + 1 have landed and nobody reads
+  //    stage s any more), issue the copies of stage s + NB into the buffer
+  //    just freed, then read the first fragments of stage s + 1.
+  // The MFMAs of a step are issued after these reads, so the barrier wait
+  // overlaps the matrix pipe still working through the previous step.
   const int KT = (K + KS - 1) / KS;
-  if constexpr (PIPE == 1) {
-    if (KT > 0) {
-      gload(0);
-      sstore(0);
-      if (KT > 1) gload(KS);
-      __syncthreads();
-      rd(0, 0, 0);
-    }
-    for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
+  // have the epilogue's kernel arguments in registers before the loop, so no
+  // scalar load is still pending inside it (that would turn every LDS wait
+  // there into a wait for all LDS reads)
+  asm volatile("" ::"s"(g.sx), "s"(g.sw), "s"(g.sw2), "s"(g.sy), "s"(g.C));
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        if (st + 1 < NSTEP) {
-          rd(buf, st + 1, (st + 1) & 1);
-        } else if (kt + 1 < KT) {
-          __syncthreads();
-          rd(buf ^ 1, 0, 0);
-        }
-        if (st == 0 && kt + 1 < KT) {
-          sstore(buf ^ 1);
-          if (kt + 2 < KT) gload((kt + 2) * KS);
-        }
-        mf(st & 1);
-      }
-    }
-  } else {
-    // single fragment set (for register-heavy tiles): each K-step reads its
-    // fragments and multiplies; the next stage is written to LDS and the one
-    // after it loaded half-way through the stage
-    if (KT > 0) {
-      gload(0);
-      sstore(0);
-      if (KT > 1) gload(KS);
-      __syncthreads();
-    }
-    for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
+  for (int u = 0; u < NB; ++u)
+    if (u < KT) issue_stage(u, u);
+  if (KT > 0) {
+    wait_copies(LPW * (min(NB, KT) - 1));
+    __syncthreads();
+    rd(0, 0, 0);
+  }
+  for (int kt0 = 0; kt0 < KT; kt0 += NB) {
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        if (st == NSTEP / 2 && kt + 1 < KT) {
-          sstore(buf ^ 1);
-          if (kt + 2 < KT) gload((kt + 2) * KS);
+    for (int u = 0; u < NB; ++u) {
+      const int s = kt0 + u;
+      if (s < KT) {
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) {
+          const int slot = (u * NSTEP + st) & 1;
+          if (st + 1 < NSTEP) {
+            rd(u, st + 1, slot ^ 1);
+            mf(slot, std::false_type{}, 0, 0);
+          } else {
+            if (s + 1 < KT) {
+              wait_copies(LPW * min(NB - 2, KT - s - 2));
+              __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+              __syncthreads();
+              rd((u + 1) % NB, 0, slot ^ 1);
+            }
+            // The copies of stage s + NB go into the buffer just freed.  Past
+            // the end of K they touch no memory and write zeros, into a
+            // buffer nobody reads again -- at the last stage, where no
+            // barrier has freed this buffer, into the next one instead.
+            mf(slot, std::true_type{}, s + 1 < KT ? u : (u + 1) % NB, s + NB);
+          }
         }
-        rd(buf, st, 0);
-        mf(0);
       }
-      __syncthreads();
     }
   }
-  __syncthreads();
+  // no copy into LDS may still be on its way when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   // ---- epilogue: y = fp32(acc * alpha), then the output format ----
+  // Accumulator register v of 32x32 block (i, j) holds row
+  // i*32 + 8*(v/4) + 4*(lane/32) + v%4, column j*32 + lane%32: the four
+  // registers v = 4q .. 4q+3 are four consecutive rows of one column, and the
+  // four lanes of a quad hold four consecutive columns.  A 4x4 transpose
+  // inside the quad (two DPP exchanges) turns that into one row-piece of four
+  // consecutive columns per lane, stored straight to global memory.
   const float alpha = __fmul_rn(*g.sx, *g.sw);
   void* __restrict__ C = g.C;
   constexpr int ESZ = OUT == 0 ? 2 : (OUT == 1 ? 1 : 4);
@@ -370,90 +462,69 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
       make_rsrc(static_cast<uint8_t*>(C) + ((int64_t)m0 * N) * ESZ, (int64_t)(M - m0) * N * ESZ);
   const int col_l = wn * WTN + (lane & 31);          // + j*32
   const int row_l = wm * WTM + (lane >> 5) * 4;       // + i*32 + 8*(v/4) + v%4
+  const int qt = lane & 3;                            // lane's place in its quad
 
   if constexpr (FUSED) {
     // G and U of one output element sit in blocks j (gate) and j + 1 (up) of
     // the same lane and register: round each to BF16 exactly as the BF16
-    // epilogue does, apply SwiGLU exactly as silu_mul_2in_fp8 does, stage the
-    // codes of the wave's [WTM x WTN/2] piece in LDS and store 16-byte rows.
+    // epilogue does, apply SwiGLU exactly as silu_mul_2in_fp8 does, encode
+    // four rows at a time, transpose the bytes in the quad and store one
+    // dword (a row's four consecutive columns) per lane.
     const float alpha_u = __fmul_rn(*g.sx, *g.sw2);
     const float rs = 1.0f / *g.sy;
-    constexpr int QW = WTN / 2;            // output columns per wave
-    constexpr int LROW = QW + 16;
-    uint8_t* wbuf = smem + wave * (WTM * LROW);
+    const __amdgpu_buffer_rsrc_t rq_rs =
+        make_rsrc(static_cast<uint8_t*>(C) + (int64_t)m0 * N, (int64_t)(M - m0) * N);
+    const int col_q = n0 + (wn * WTN) / 2 + ((lane & 31) & ~3);   // + p*32
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int p = 0; p < FN / 2; ++p)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          const int c = p * 32 + (lane & 31);
-          const float yg = __fmul_rn(acc[i][2 * p][v], alpha);
-          const float yu = __fmul_rn(acc[i][2 * p + 1][v], alpha_u);
-          const float h = silu_mul(bf16_to_f32(f32_to_bf16(yg)), bf16_to_f32(f32_to_bf16(yu)));
-          wbuf[r * LROW + c] = (uint8_t)e4m3_encode(__fmul_rn(h, rs));
-        }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
-    __builtin_amdgcn_wave_barrier();
-    constexpr int PIECES = QW / 16;
-    const __amdgpu_buffer_rsrc_t rq_rs =
-        make_rsrc(static_cast<uint8_t*>(C) + (int64_t)m0 * N, (int64_t)(M - m0) * N);
+        for (int q = 0; q < 4; ++q) {
+          float h[4];
 #pragma unroll
-    for (int p = lane; p < WTM * PIECES; p += 64) {
-      const int r = p / PIECES, c16 = (p % PIECES) * 16;
-      const v4i val = *reinterpret_cast<const v4i*>(wbuf + r * LROW + c16);
-      const int grow = wm * WTM + r;                           // row within tile
-      const int gcol = n0 + (wn * WTN) / 2 + c16;              // output column
-      const int off = (m0 + grow < M && gcol < N) ? grow * N + gcol : kOOB;
-      __builtin_amdgcn_raw_buffer_store_b128(val, rq_rs, off, 0, 0);
-    }
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * q + e;
+            const uint32_t gu = bf16x2_rne(__fmul_rn(acc[i][2 * p][v], alpha),
+                                           __fmul_rn(acc[i][2 * p + 1][v], alpha_u));
+            h[e] = __fmul_rn(silu_mul(__uint_as_float(gu << 16), __uint_as_float(gu & 0xFFFF0000u)), rs);
+          }
+          const uint32_t w = quad_transpose_bytes(e4m3_pack4(h[0], h[1], h[2], h[3]), qt);
+          const int row = row_l + i * 32 + q * 8 + qt;       // row within tile
+          const int col = col_q + p * 32;
+          const int off = (m0 + row < M && col < N) ? row * N + col : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b32(w, rq_rs, off, 0, 0);
+        }
   } else if constexpr (OUT == 0) {
-    // BF16: each wave stages half of its sub-tile at a time in LDS (rows of
-    // WTN values, padded by 16 bytes so the two row groups a store
-    // instruction writes fall in different banks), then writes whole
-    // 16-byte row pieces with coalesced stores.
-    constexpr int LROW = WTN * 2 + 16;
-    constexpr int HALF = FM / 2 > 0 ? FM / 2 : 1;
-    uint8_t* wbuf = smem + wave * (HALF * 32 * LROW);
-    const bool vec_ok = (N % 8) == 0;
+    // BF16: four rows of a column -> two packed dwords, transposed in the
+    // quad so that each lane stores four consecutive columns of one row
+    // (8 bytes).  Rows whose width is not a multiple of 4 take 2-byte stores.
+    const bool vec_ok = (N % 4) == 0;
+    const int col_q = n0 + wn * WTN + ((lane & 31) & ~3);   // + j*32
 #pragma unroll
-    for (int h = 0; h < FM / HALF; ++h) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int ii = 0; ii < HALF; ++ii)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t a = bf16x2_rne(__fmul_rn(acc[i][j][4 * q + 0], alpha), __fmul_rn(acc[i][j][4 * q + 1], alpha));
+          const uint32_t b = bf16x2_rne(__fmul_rn(acc[i][j][4 * q + 2], alpha), __fmul_rn(acc[i][j][4 * q + 3], alpha));
+          uint32_t d0, d1;
+          quad_transpose_halves(a, b, qt, d0, d1);
+          const int row = row_l + i * 32 + q * 8 + qt;
+          const int col = col_q + j * 32;
+          if (vec_ok) {
+            const int off = (m0 + row < M && col < N) ? (row * N + col) * 2 : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b64((v2u){d0, d1}, rc_rs, off, 0, 0);
+          } else {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = ii * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-            const int c = j * 32 + (lane & 31);
-            const float y = __fmul_rn(acc[h * HALF + ii][j][v], alpha);
-            *reinterpret_cast<uint16_t*>(wbuf + r * LROW + c * 2) = (uint16_t)f32_to_bf16(y);
-          }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
-      __builtin_amdgcn_wave_barrier();
-      constexpr int PIECES = WTN / 8;          // 16-byte pieces per row
-      constexpr int ROWS = HALF * 32;
-#pragma unroll
-      for (int p = lane; p < ROWS * PIECES; p += 64) {
-        const int r = p / PIECES, c8 = (p % PIECES) * 8;
-        const v4i val = *reinterpret_cast<const v4i*>(wbuf + r * LROW + c8 * 2);
-        const int grow = wm * WTM + (h * HALF) * 32 + r;   // row within tile
-        const int gcol = n0 + wn * WTN + c8;
-        if (vec_ok) {
-          const int off = (m0 + grow < M && gcol < N) ? (grow * N + gcol) * 2 : kOOB;
-          __builtin_amdgcn_raw_buffer_store_b128(val, rc_rs, off, 0, 0);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int off = (m0 + grow < M && gcol + e < N) ? (grow * N + gcol + e) * 2 : kOOB;
-            const uint16_t hv = (uint16_t)((uint32_t)val[e >> 1] >> ((e & 1) * 16));
-            __builtin_amdgcn_raw_buffer_store_b16(hv, rc_rs, off, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+              const int off = (m0 + row < M && col + e < N) ? (row * N + col + e) * 2 : kOOB;
+              const uint32_t d = e < 2 ? d0 : d1;
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(d >> ((e & 1) * 16)), rc_rs, off, 0, 0);
+            }
           }
         }
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
   } else {
     const float sy = (OUT == 1) ? *g.sy : 1.0f;
 #pragma unroll
@@ -476,11 +547,6 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
-// Pipeline style: double-buffered fragments (1) except for the FP8 engine with
-// 8 waves, whose 32-byte fragments would not fit twice in 256 registers (0).
-template <int ENGINE, int WAVES>
-constexpr int kPipe = (ENGINE == 1 && WAVES == 8) ? 0 : 1;
-
 template <int BM, int BN, int WM, int WN, int ENGINE>
 hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
   a.tiles_m = (a.M + BM - 1) / BM;
@@ -488,13 +554,13 @@ hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
   const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
   switch (out_kind) {
     case 0:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE, false, kPipe<ENGINE, WM * WN>>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE, false>), grid, block, 0, stream, a);
       break;
     case 1:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false, kPipe<ENGINE, WM * WN>>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false>), grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false, kPipe<ENGINE, WM * WN>>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false>), grid, block, 0, stream, a);
       break;
   }
   return hipGetLastError();
@@ -505,7 +571,7 @@ hipError_t launch_fused(GemmArgs a, hipStream_t stream) {
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + 127) / 128;
   const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
-  hipLaunchKernelGGL((gemm_kernel<BM, 256, WM, WN, 0, ENGINE, true, kPipe<ENGINE, WM * WN>>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, 256, WM, WN, 0, ENGINE, true>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -558,3 +624,4 @@ hipError_t launch_gemm_swiglu(const uint8_t* qx, const uint8_t* wg, const uint8_
 }
 
 }  // namespace fp8mot
+
