@@ -22,7 +22,9 @@ formats   E4M3 (OCP E4M3FN) decode/encode and BF16 rounding.
 linear    static activation quantization, RTN weight quantization, the exact
           FP8 GEMM and its epilogues, and the fused-group re-quantization
           failure mode.
-swiglu    two-input SiLU(G)*U with direct FP8 emission.
+swiglu    two-input SiLU(G)*U with direct FP8 emission; the alpha (gain inside
+          the sigmoid) / beta (offset on up) variant and the one-input form
+          with gate and up adjacent in one tensor.
 observer  per-call amax and the max / moving-average observers.
 
 Every function here is pinned by a ``-m "not gpu"`` test in ``tests/`` to
