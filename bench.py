@@ -228,7 +228,8 @@ def main():
 
 def elementwise_large(fp8, torch, dev, stream):
     """The HBM-bound kernels at the large gated-MLP sizes (X [16384, 5120],
-    G/U [16384, 25600]), where the working sets exceed the 256 MB MALL:
+    G/U [16384, 25600], or G|U adjacent in one [16384, 51200] tensor for the
+    one-input SwiGLU), where the working sets exceed the 256 MB MALL:
     average launch time over back-to-back launches (three rotating X copies
     for quantize), algorithmic GB/s, and the fraction of the 8 TB/s peak.
     A plain device copy of the SwiGLU's byte count is timed beside them."""
@@ -261,12 +262,24 @@ def elementwise_large(fp8, torch, dev, stream):
     us = timed(lambda r: fp8.silu_mul_2in_fp8(g, u, s, out=q), 8)
     out["silu_16384x25600"] = {"us": us, "bytes": 5 * n, "GB/s": 5 * n / us / 1e3,
                                "frac_hbm": 5 * n / us / 1e3 / HBM_PEAK_GBS}
+    # the swiglu_alpha / swiglu_beta variant (swigluoai shape) on the same data
+    us = timed(lambda r: fp8.silu_mul_2in_fp8(g, u, s, out=q, alpha=1.702, beta=1.0), 8)
+    out["silu_ab_16384x25600"] = {"us": us, "bytes": 5 * n, "GB/s": 5 * n / us / 1e3,
+                                  "frac_hbm": 5 * n / us / 1e3 / HBM_PEAK_GBS}
     del q
     a = g.view(torch.uint8)
     b = torch.empty_like(a)
     us = timed(lambda r: b.copy_(a), 8)
     out["device_copy_same_bytes"] = {"us": us, "GB/s": 2 * a.numel() / us / 1e3}
     del g, u, a, b
+    torch.cuda.empty_cache()
+    # one-input SwiGLU: gate and up adjacent in one [16384, 2 x 25600] tensor
+    x = torch.randn((16384, 2 * 25600), device=dev).to(torch.bfloat16)
+    q = torch.empty((16384, 25600), dtype=torch.uint8, device=dev)
+    us = timed(lambda r: fp8.silu_mul_fp8(x, s, out=q), 8)
+    out["silu_1in_16384x25600"] = {"us": us, "bytes": 5 * n, "GB/s": 5 * n / us / 1e3,
+                                   "frac_hbm": 5 * n / us / 1e3 / HBM_PEAK_GBS}
+    del x, q
     torch.cuda.empty_cache()
     return out
 

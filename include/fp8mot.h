@@ -162,6 +162,30 @@ int fp8_linear(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
 int silu_mul_2in_fp8(const uint16_t* g, const uint16_t* u, uint8_t* q,
                      int64_t n, const float* d_s_out, hipStream_t stream);
 
+/* The same with the swiglu_alpha / swiglu_beta variant ([PR] commit message
+ * on swiglu_alpha / swiglu_beta: alpha is a gain inside the sigmoid, beta an
+ * offset on up):
+ *   q[i] = e4m3(g[i] * sigmoid(alpha * g[i]) * (u[i] + beta) / *d_s_out)
+ * in FP32.  A zero beta leaves u untouched, so (alpha, beta) = (1, 0) gives
+ * exactly the codes of silu_mul_2in_fp8.  Non-finite alpha or beta is
+ * FP8MOT_ERR_INVALID_ARG; other arguments as silu_mul_2in_fp8. */
+int silu_mul_2in_fp8_ab(const uint16_t* g, const uint16_t* u, uint8_t* q,
+                        int64_t n, const float* d_s_out, float alpha, float beta,
+                        hipStream_t stream);
+
+/* One-input SwiGLU with gate and up adjacent in one tensor ([PR] commit
+ * message: silu_and_mul needs gate and up adjacent; the two-input form exists
+ * because separate projections have no such tensor).  x: BF16 [rows, 2*inter]
+ * whose row r holds the inter gate values, then the inter up values;
+ * q: E4M3 [rows, inter]:
+ *   q[r, c] = e4m3(g * sigmoid(alpha g) * (u + beta) / *d_s_out),
+ *   g = x[r, c], u = x[r, inter + c],
+ * bit for bit what silu_mul_2in_fp8_ab gives on the two halves.  x and q
+ * 16-byte aligned (FP8MOT_ERR_MISALIGNED); rows, inter >= 0; any inter (a
+ * multiple of 16 takes the vector path). */
+int silu_mul_fp8(const uint16_t* x, uint8_t* q, int64_t rows, int64_t inter,
+                 const float* d_s_out, float alpha, float beta, hipStream_t stream);
+
 /* ------------------------------------------------------------------ */
 /* Composites (one shared quantization, contiguous outputs, no sync)   */
 /* ------------------------------------------------------------------ */

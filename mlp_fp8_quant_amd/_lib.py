@@ -25,6 +25,10 @@ SIGNATURES = {
                            c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p]),
     "silu_mul_2in_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_void_p,
                                  c_void_p]),
+    "silu_mul_2in_fp8_ab": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_void_p,
+                                    c_float, c_float, c_void_p]),
+    "silu_mul_fp8": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_void_p,
+                             c_float, c_float, c_void_p]),
     "gated_mlp_fp8_workspace": (c_size_t, [c_i64, c_i64, c_i64]),
     "gated_mlp_fp8": (c_int, [c_void_p, c_i64, c_i64, c_i64, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -97,8 +97,10 @@ def fp8_linear(qx, qw, sx, sw, out_kind=OUT_BF16, sy=None, out=None,
     return out
 
 
-def silu_mul_2in_fp8(g, u, s_out, out=None):
-    """E4M3 codes of silu(g) * u at ``s_out``; g and u BF16 of equal shape."""
+def silu_mul_2in_fp8(g, u, s_out, out=None, alpha=None, beta=None):
+    """E4M3 codes of g * sigmoid(alpha g) * (u + beta) at ``s_out``; g and u
+    BF16 of equal shape.  Without alpha and beta this is plain SwiGLU
+    (silu(g) * u); alpha is a gain inside the sigmoid, beta an offset on up."""
     _need(g, "g", torch.bfloat16)
     _need(u, "u", torch.bfloat16, g.device)
     if g.shape != u.shape:
@@ -109,8 +111,35 @@ def silu_mul_2in_fp8(g, u, s_out, out=None):
     _need(out, "out", torch.uint8, g.device)
     if out.numel() != g.numel():
         raise ValueError("out must have as many elements as g")
-    _lib.call("silu_mul_2in_fp8", _ptr(g), _ptr(u), _ptr(out), g.numel(),
-              _ptr(s_out), _stream(g))
+    if alpha is None and beta is None:
+        _lib.call("silu_mul_2in_fp8", _ptr(g), _ptr(u), _ptr(out), g.numel(),
+                  _ptr(s_out), _stream(g))
+    else:
+        _lib.call("silu_mul_2in_fp8_ab", _ptr(g), _ptr(u), _ptr(out), g.numel(),
+                  _ptr(s_out), 1.0 if alpha is None else float(alpha),
+                  0.0 if beta is None else float(beta), _stream(g))
+    return out
+
+
+def silu_mul_fp8(x, s_out, out=None, alpha=None, beta=None):
+    """One-input SwiGLU-FP8: x BF16 [..., 2I] whose rows hold the I gate values
+    followed by the I up values; returns E4M3 codes [..., I] of
+    g * sigmoid(alpha g) * (u + beta) at ``s_out`` (alpha 1, beta 0 when
+    omitted), bit for bit what silu_mul_2in_fp8 gives on the two halves."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() == 0 or x.shape[-1] % 2:
+        raise ValueError("x must end in an even dimension [..., 2I]")
+    _scale(s_out, "s_out", x.device)
+    inter = x.shape[-1] // 2
+    rows = math.prod(x.shape[:-1])
+    if out is None:
+        out = torch.empty((*x.shape[:-1], inter), dtype=torch.uint8, device=x.device)
+    _need(out, "out", torch.uint8, x.device)
+    if out.numel() != rows * inter:
+        raise ValueError("out must hold [..., I] elements")
+    _lib.call("silu_mul_fp8", _ptr(x), _ptr(out), rows, inter, _ptr(s_out),
+              1.0 if alpha is None else float(alpha),
+              0.0 if beta is None else float(beta), _stream(x))
     return out
 
 

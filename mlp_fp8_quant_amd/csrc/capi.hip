@@ -136,17 +136,39 @@ int fp8_linear(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
   return hip_status(launch_gemm(qx, qw, y, M, N, K, d_sx, d_sw, out_kind, d_sy, accum, cus, stream));
 }
 
-int silu_mul_2in_fp8(const uint16_t* g, const uint16_t* u, uint8_t* q,
-                     int64_t n, const float* d_s_out, hipStream_t stream) {
+int silu_mul_2in_fp8_ab(const uint16_t* g, const uint16_t* u, uint8_t* q,
+                        int64_t n, const float* d_s_out, float alpha, float beta,
+                        hipStream_t stream) {
   if (d_s_out == nullptr) return FP8MOT_ERR_UNSUPPORTED;
-  if (n < 0) return FP8MOT_ERR_INVALID_ARG;
+  if (n < 0 || !std::isfinite(alpha) || !std::isfinite(beta)) return FP8MOT_ERR_INVALID_ARG;
   if (n == 0) return FP8MOT_OK;
   if (g == nullptr || u == nullptr || q == nullptr) return FP8MOT_ERR_INVALID_ARG;
   if (!aligned16(g) || !aligned16(u) || !aligned16(q)) return FP8MOT_ERR_MISALIGNED;
   int cus = 0;
   int st = current_device(&cus);
   if (st != FP8MOT_OK) return st;
-  return hip_status(launch_silu_mul(g, u, q, n, d_s_out, ew_blocks(cus), stream));
+  return hip_status(launch_silu_mul(g, u, q, n, d_s_out, alpha, beta, ew_blocks(cus), stream));
+}
+
+int silu_mul_2in_fp8(const uint16_t* g, const uint16_t* u, uint8_t* q,
+                     int64_t n, const float* d_s_out, hipStream_t stream) {
+  return silu_mul_2in_fp8_ab(g, u, q, n, d_s_out, 1.0f, 0.0f, stream);
+}
+
+int silu_mul_fp8(const uint16_t* x, uint8_t* q, int64_t rows, int64_t inter,
+                 const float* d_s_out, float alpha, float beta, hipStream_t stream) {
+  if (d_s_out == nullptr) return FP8MOT_ERR_UNSUPPORTED;
+  if (rows < 0 || inter < 0 || !std::isfinite(alpha) || !std::isfinite(beta))
+    return FP8MOT_ERR_INVALID_ARG;
+  if (rows > 0 && inter > INT64_MAX / 2 / rows) return FP8MOT_ERR_INVALID_ARG;
+  if (rows == 0 || inter == 0) return FP8MOT_OK;
+  if (x == nullptr || q == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(q)) return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_silu_mul_adjacent(x, q, rows, inter, d_s_out, alpha, beta,
+                                             ew_blocks(cus), stream));
 }
 
 size_t gated_mlp_fp8_workspace(int64_t M, int64_t H, int64_t I) {

@@ -80,4 +80,16 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return __fmul_rn(s, u);
 }
 
+// The SwiGLU variant of the pull request "Load static FP8 Cosmos3 Nano/Super
+// checkpoints without re-quantizing them" (commit message on swiglu_alpha /
+// swiglu_beta): alpha is a gain inside the sigmoid, beta an offset on up,
+// g * sigmoid(alpha * g) * (u + beta).  A zero beta leaves u untouched (so a
+// -0 stays -0) and 1 * g == g exactly, so (alpha, beta) = (1, 0) gives the
+// bits of silu_mul.
+__device__ __forceinline__ float silu_mul_ab(float g, float u, float alpha, float beta) {
+  const float e = __expf(-__fmul_rn(alpha, g));
+  const float s = __fmul_rn(g, __builtin_amdgcn_rcpf(__fadd_rn(1.0f, e)));
+  return __fmul_rn(s, beta == 0.0f ? u : __fadd_rn(u, beta));
+}
+
 }  // namespace fp8mot

@@ -1,5 +1,6 @@
-// HBM-bound kernels of libfp8mot: static activation quantization, two-input
-// SwiGLU with FP8 output, and the amax observer.
+// HBM-bound kernels of libfp8mot: static activation quantization, SwiGLU with
+// FP8 output (two-input, and one-input with gate and up adjacent), and the
+// amax observer.
 //
 // All three stream flat contiguous buffers with 128-bit nontemporal loads and
 // stores, several in flight per thread; the grid strides over 16-element
@@ -74,18 +75,33 @@ __global__ __launch_bounds__(kThreads) void quant_static_kernel(
   }
 }
 
-// Two-input SwiGLU: q = e4m3(silu(g) * u / s_out), the division done as a
-// multiplication by the (correctly rounded) reciprocal of s_out.  A thread
-// handles 32 elements per step: eight 128-bit loads in flight, two stores.
+// SwiGLU with FP8 output: q = e4m3(g * sigmoid(alpha g) * (u + beta) / s_out),
+// the division done as a multiplication by the (correctly rounded)
+// reciprocal of s_out.  A thread handles 32 elements per step: eight 128-bit
+// loads in flight, two stores.
+//  ADJ = false: g and u are two flat tensors of n elements (two-input form).
+//  ADJ = true:  one tensor x of rows [gate (I) | up (I)], I % 16 == 0; the
+//               output is [rows, I] and n = rows * I.  Each 16-element unit
+//               lies inside one row half.
+template <bool ADJ>
 __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ u,
-    uint8_t* __restrict__ q, int64_t n, const float* __restrict__ d_s) {
+    uint8_t* __restrict__ q, int64_t n, const float* __restrict__ d_s,
+    float alpha, float beta, uint32_t inter) {
   const float rs = 1.0f / *d_s;
   const int64_t units = n >> 4;
   const int64_t stride = (int64_t)gridDim.x * kThreads * 2;
-  const u32x4* gv = reinterpret_cast<const u32x4*>(g);
-  const u32x4* uv = reinterpret_cast<const u32x4*>(u);
+  const uint32_t upr = inter >> 4;              // ADJ: units per row
   u32x4* qv = reinterpret_cast<u32x4*>(q);
+  // element offset of unit i's gate values (its up values follow at +inter)
+  auto gate_at = [&](int64_t i) -> int64_t {
+    if constexpr (ADJ) {
+      const uint32_t r = (uint32_t)i / upr, c = (uint32_t)i - r * upr;
+      return (int64_t)r * (2 * (int64_t)inter) + 16 * (int64_t)c;
+    } else {
+      return 16 * i;
+    }
+  };
   for (int64_t base = (int64_t)blockIdx.x * kThreads * 2 + threadIdx.x; base < units;
        base += stride) {
     u32x4 a[2][4];
@@ -93,10 +109,13 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
     for (int k = 0; k < 2; ++k) {
       const int64_t i = base + k * kThreads;
       if (i < units) {
-        a[k][0] = __builtin_nontemporal_load(gv + 2 * i);
-        a[k][1] = __builtin_nontemporal_load(gv + 2 * i + 1);
-        a[k][2] = __builtin_nontemporal_load(uv + 2 * i);
-        a[k][3] = __builtin_nontemporal_load(uv + 2 * i + 1);
+        const int64_t e = gate_at(i);
+        const u32x4* gp = reinterpret_cast<const u32x4*>(g + e);
+        const u32x4* up = reinterpret_cast<const u32x4*>(ADJ ? g + e + inter : u + e);
+        a[k][0] = __builtin_nontemporal_load(gp);
+        a[k][1] = __builtin_nontemporal_load(gp + 1);
+        a[k][2] = __builtin_nontemporal_load(up);
+        a[k][3] = __builtin_nontemporal_load(up + 1);
       }
     }
 #pragma unroll
@@ -110,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
         unpack8(a[k][3], fu + 8);
         float h[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) h[j] = __fmul_rn(silu_mul(fg[j], fu[j]), rs);
+        for (int j = 0; j < 16; ++j) h[j] = __fmul_rn(silu_mul_ab(fg[j], fu[j], alpha, beta), rs);
         u32x4 o;
         o.x = e4m3_pack4(h[0], h[1], h[2], h[3]);
         o.y = e4m3_pack4(h[4], h[5], h[6], h[7]);
@@ -120,10 +139,26 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
       }
     }
   }
-  if (blockIdx.x == 0) {
+  if (!ADJ && blockIdx.x == 0) {
     const int64_t t = (units << 4) + threadIdx.x;
     if (t < n)
-      q[t] = (uint8_t)e4m3_encode(__fmul_rn(silu_mul(bf16_to_f32(g[t]), bf16_to_f32(u[t])), rs));
+      q[t] = (uint8_t)e4m3_encode(
+          __fmul_rn(silu_mul_ab(bf16_to_f32(g[t]), bf16_to_f32(u[t]), alpha, beta), rs));
+  }
+}
+
+// One-input SwiGLU for rows whose width I is not a multiple of 16: one
+// element per thread per step (such rows are not 16-byte aligned).
+__global__ __launch_bounds__(kThreads) void silu_mul_adj_scalar_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int64_t n,
+    const float* __restrict__ d_s, float alpha, float beta, int64_t inter) {
+  const float rs = 1.0f / *d_s;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = e / inter, c = e - r * inter;
+    const uint16_t* row = x + r * 2 * inter;
+    q[e] = (uint8_t)e4m3_encode(
+        __fmul_rn(silu_mul_ab(bf16_to_f32(row[c]), bf16_to_f32(row[inter + c]), alpha, beta), rs));
   }
 }
 
@@ -260,10 +295,25 @@ hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
 }
 
 hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
-                           int64_t n, const float* d_s, int max_blocks,
-                           hipStream_t stream) {
-  hipLaunchKernelGGL(silu_mul_kernel, dim3(grid_for(n >> 5, max_blocks)),
-                     dim3(kThreads), 0, stream, g, u, q, n, d_s);
+                           int64_t n, const float* d_s, float alpha, float beta,
+                           int max_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(grid_for(n >> 5, max_blocks)),
+                     dim3(kThreads), 0, stream, g, u, q, n, d_s, alpha, beta, 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_adjacent(const uint16_t* x, uint8_t* q, int64_t rows,
+                                    int64_t inter, const float* d_s, float alpha,
+                                    float beta, int max_blocks, hipStream_t stream) {
+  const int64_t n = rows * inter;
+  if (inter % 16 == 0 && n / 16 <= (int64_t)UINT32_MAX) {
+    hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(grid_for(n >> 5, max_blocks)),
+                       dim3(kThreads), 0, stream, x, nullptr, q, n, d_s, alpha, beta,
+                       (uint32_t)inter);
+  } else {
+    hipLaunchKernelGGL(silu_mul_adj_scalar_kernel, dim3(grid_for(n, 4 * max_blocks)),
+                       dim3(kThreads), 0, stream, x, q, n, d_s, alpha, beta, inter);
+  }
   return hipGetLastError();
 }
 

@@ -20,9 +20,16 @@ hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                                const float* d_scale, int max_blocks,
                                hipStream_t stream);
 
+// q = e4m3(g * sigmoid(alpha g) * (u + beta) / s); (1, 0) is plain SwiGLU.
 hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
-                           int64_t n, const float* d_s, int max_blocks,
-                           hipStream_t stream);
+                           int64_t n, const float* d_s, float alpha, float beta,
+                           int max_blocks, hipStream_t stream);
+
+// The same from one tensor x of rows [gate (inter) | up (inter)] into
+// q [rows, inter].
+hipError_t launch_silu_mul_adjacent(const uint16_t* x, uint8_t* q, int64_t rows,
+                                    int64_t inter, const float* d_s, float alpha,
+                                    float beta, int max_blocks, hipStream_t stream);
 
 // u == nullptr: amax of the BF16 tensor x; otherwise amax of silu(x) * u.
 hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,

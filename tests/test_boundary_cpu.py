@@ -30,7 +30,8 @@ def test_header_declares_the_hot_path_calls():
     names = declared_functions()
     for n in ("fp8_quant_static", "fp8_linear", "silu_mul_2in_fp8",
               "gated_mlp_fp8", "qkv_fp8", "fp8_observe", "fp8_scale_from_state",
-              "fp8_check_shared_scale", "fp8_gate_up_swiglu"):
+              "fp8_check_shared_scale", "fp8_gate_up_swiglu",
+              "silu_mul_2in_fp8_ab", "silu_mul_fp8"):
         assert n in names
 
 
@@ -116,3 +117,32 @@ def test_refusals_before_any_device_access():
     assert lib.fp8_linear(fake, fake, fake, 4, 4, 16, s, s, 0, null, 2, null) == 1
     assert lib.gated_mlp_fp8(fake, 4, 16, 32, s, fake, s, fake, s, s, fake, s,
                              fake, fake, 1 << 20, 5, null) == 1
+
+
+def test_swiglu_variant_refusals_before_any_device_access():
+    lib = _lib()
+    P = ctypes.c_void_p
+    fake = P(0x10000)        # never dereferenced: every case below is refused
+    odd = P(0x10001)
+    null = P(0)
+    s = fake
+    nan, inf = float("nan"), float("inf")
+    # NULL scale -> UNSUPPORTED
+    assert lib.silu_mul_2in_fp8_ab(fake, fake, fake, 16, null, 1.0, 0.0, null) == 4
+    assert lib.silu_mul_fp8(fake, fake, 2, 16, null, 1.0, 0.0, null) == 4
+    # non-finite alpha / beta, negative sizes -> INVALID_ARG
+    assert lib.silu_mul_2in_fp8_ab(fake, fake, fake, 16, s, nan, 0.0, null) == 1
+    assert lib.silu_mul_2in_fp8_ab(fake, fake, fake, 16, s, 1.0, inf, null) == 1
+    assert lib.silu_mul_2in_fp8_ab(fake, fake, fake, -1, s, 1.0, 0.0, null) == 1
+    assert lib.silu_mul_fp8(fake, fake, 2, 16, s, inf, 0.0, null) == 1
+    assert lib.silu_mul_fp8(fake, fake, -2, 16, s, 1.0, 0.0, null) == 1
+    assert lib.silu_mul_fp8(fake, fake, 2, -16, s, 1.0, 0.0, null) == 1
+    assert lib.silu_mul_fp8(null, fake, 2, 16, s, 1.0, 0.0, null) == 1
+    # empty -> OK without touching anything
+    assert lib.silu_mul_2in_fp8_ab(null, null, null, 0, s, 1.0, 0.0, null) == 0
+    assert lib.silu_mul_fp8(null, null, 0, 16, s, 1.0, 0.0, null) == 0
+    assert lib.silu_mul_fp8(null, null, 3, 0, s, 1.0, 0.0, null) == 0
+    # misaligned -> MISALIGNED
+    assert lib.silu_mul_2in_fp8_ab(fake, odd, fake, 16, s, 1.0, 0.0, null) == 2
+    assert lib.silu_mul_fp8(odd, fake, 2, 16, s, 1.0, 0.0, null) == 2
+    assert lib.silu_mul_fp8(fake, odd, 2, 16, s, 1.0, 0.0, null) == 2
