@@ -50,9 +50,9 @@ int current_device(int* cus) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8MOT_OK : FP8MOT_ERR_HIP; }
 
-// Blocks for the grid-stride elementwise kernels: 8 workgroups per CU, each
-// thread keeping four to eight 128-bit loads in flight (measured on MI355X:
-// more workgroups made the read-write kernels slower).
+// Workgroup budget of the grid-stride elementwise kernels: 8 per CU.  The
+// launchers scale it per kernel (quantize and SwiGLU use twice as many, the
+// amax reductions a quarter), as measured on MI355X.
 int ew_blocks(int cus) { return cus * 8; }
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
