@@ -26,6 +26,7 @@ swiglu    two-input SiLU(G)*U with direct FP8 emission; the alpha (gain inside
           the sigmoid) / beta (offset on up) variant and the one-input form
           with gate and up adjacent in one tensor.
 observer  per-call amax and the max / moving-average observers.
+rowwise   per-row FP8: per-channel weight and per-token activation scales.
 
 Every function here is pinned by a ``-m "not gpu"`` test in ``tests/`` to
 something other than itself (closed forms, library conversions, exact integer
@@ -33,4 +34,4 @@ arithmetic, brute force).  A function without such a pin would be listed here
 as "parity unpinned"; at present there is none.
 """
 
-from . import formats, linear, observer, swiglu  # noqa: F401
+from . import formats, linear, observer, rowwise, swiglu  # noqa: F401
