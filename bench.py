@@ -198,6 +198,7 @@ def main():
     }
 
     large = None if args.no_large else elementwise_large(fp8, torch, dev, stream)
+    rowwise = None if args.no_large else per_row_fp8(fp8, torch, dev, stream, M, H, I)
 
     if args.copy_calib_mb > 0:
         n = args.copy_calib_mb << 20
@@ -221,9 +222,52 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
         "fp8_mfma_engine": fp8_engine,
         "elementwise_large": large,
+        "per_row_fp8": rowwise,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out))
+
+
+def per_row_fp8(fp8, torch, dev, stream, M, H, I):
+    """Per-row FP8 (per-token activation / per-channel weight scales) beside
+    the per-tensor path: per-token quantization of the gen MLP's X [M, H] and of
+    the large MLP's X [16384, 5120] (3 B per element), and the gate projection
+    [M, I, H] with per-row scales on both engines (TFLOP/s)."""
+    def timed(f, reps):
+        for r in range(2):
+            f(r)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            f(r)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {}
+    for rows, k, reps in ((M, H, 50), (16384, 5120, 20)):
+        xs = [torch.randn((rows, k), device=dev).to(torch.bfloat16) for _ in range(3)]
+        q = torch.empty((rows, k), dtype=torch.uint8, device=dev)
+        sc = torch.empty(rows, dtype=torch.float32, device=dev)
+        us = timed(lambda r: fp8.fp8_quant_per_row(xs[r % 3], out=q, scales=sc), reps)
+        out[f"quant_per_row_{rows}x{k}"] = {"us": us, "bytes": 3 * rows * k,
+                                            "GB/s": 3 * rows * k / us / 1e3,
+                                            "frac_hbm": 3 * rows * k / us / 1e3 / HBM_PEAK_GBS}
+        del xs, q, sc
+    x = torch.randn((M, H), device=dev).to(torch.bfloat16)
+    w = (torch.randn((I, H), device=dev) * 0.02).to(torch.bfloat16)
+    qx, sx = fp8.fp8_quant_per_row(x)
+    qw, sw = fp8.fp8_quant_per_row(w)
+    y = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    fl = 2.0 * M * I * H
+    for eng, name in ((fp8.ACC_EXACT, "exact"), (fp8.ACC_FP8_MFMA, "fp8_mfma")):
+        us = timed(lambda r: fp8.fp8_linear_rowwise(qx, qw, sx, sw, out=y, accum=eng), 20)
+        out[f"linear_rowwise_{name}_{M}x{I}x{H}"] = {"us": us, "TFLOP/s": fl / us / 1e6}
+    del x, w, qx, qw, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def elementwise_large(fp8, torch, dev, stream):

@@ -187,6 +187,36 @@ int silu_mul_fp8(const uint16_t* x, uint8_t* q, int64_t rows, int64_t inter,
                  const float* d_s_out, float alpha, float beta, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
+/* Per-row FP8 (per-channel weights, per-token activations)            */
+/* ------------------------------------------------------------------ */
+
+/* Per-row dynamic quantization ([MC] section 3.2: the per-channel weight /
+ * per-token activation builds; the runtime FP8 path quantizes weights per
+ * output channel at load and activations per token at run time).  For each
+ * row r of x (BF16 [rows, K]):
+ *   d_scales[r] = fp32(max_k |x[r,k]|) / 448      (FP32 division)
+ *   q[r,k]      = e4m3(fp32(x[r,k]) / d_scales[r]) (IEEE FP32 division)
+ * A zero row gets scale 0 and keeps its signed zeros; a row holding a NaN
+ * gets a NaN scale and NaN codes.  Used for per-token activations (rows =
+ * tokens) and, at load time, per-channel weights (rows = output channels).
+ * K must be a multiple of 16 (FP8MOT_ERR_INVALID_ARG); x, q 16-byte aligned
+ * (FP8MOT_ERR_MISALIGNED); d_scales: FP32 [rows], caller-owned device memory.
+ * rows == 0 or K == 0 does nothing. */
+int fp8_quant_per_row(const uint16_t* x, uint8_t* q, float* d_scales,
+                      int64_t rows, int64_t K, hipStream_t stream);
+
+/* FP8 GEMM with per-row scales on both operands:
+ *   y[m,n] = fp32( acc[m,n] * fp32(d_sx[m] * d_sw[n]) ),
+ *   acc[m,n] = sum_k dec(qx[m,k]) * dec(qw[n,k])   (engine per `accum`)
+ * d_sx: FP32 [M] (per token), d_sw: FP32 [N] (per output channel), both
+ * device memory, 16-byte aligned.  out_kind: FP8MOT_OUT_BF16 or
+ * FP8MOT_OUT_F32 (FP8 output is FP8MOT_ERR_UNSUPPORTED).  Other arguments and
+ * refusals as fp8_linear. */
+int fp8_linear_rowwise(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
+                       int64_t N, int64_t K, const float* d_sx, const float* d_sw,
+                       int out_kind, int accum, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
 /* Composites (one shared quantization, contiguous outputs, no sync)   */
 /* ------------------------------------------------------------------ */
 

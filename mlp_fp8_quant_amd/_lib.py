@@ -23,6 +23,9 @@ SIGNATURES = {
     "fp8_quant_static": (c_int, [c_void_p, c_void_p, c_i64, c_void_p, c_void_p]),
     "fp8_linear": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64,
                            c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p]),
+    "fp8_quant_per_row": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p]),
+    "fp8_linear_rowwise": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64,
+                                   c_void_p, c_void_p, c_int, c_int, c_void_p]),
     "silu_mul_2in_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_void_p,
                                  c_void_p]),
     "silu_mul_2in_fp8_ab": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_void_p,

@@ -97,6 +97,58 @@ def fp8_linear(qx, qw, sx, sw, out_kind=OUT_BF16, sy=None, out=None,
     return out
 
 
+def fp8_quant_per_row(x, out=None, scales=None):
+    """Per-row dynamic FP8 quantization of a BF16 [..., K] tensor (K % 16 ==
+    0): returns (codes [..., K], FP32 scales [...]) with scale = amax(row) /
+    448 and codes = e4m3(x / scale) -- per-token activations, or per-channel
+    weights at load."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() == 0:
+        raise ValueError("x must have a last (K) dimension")
+    K = x.shape[-1]
+    rows = math.prod(x.shape[:-1])
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _need(out, "out", torch.uint8, x.device)
+    _need(scales, "scales", torch.float32, x.device)
+    if out.numel() != x.numel() or scales.numel() != rows:
+        raise ValueError("out must match x and scales must hold one value per row")
+    _lib.call("fp8_quant_per_row", _ptr(x), _ptr(out), _ptr(scales), rows, K,
+              _stream(x))
+    return out, scales
+
+
+def fp8_linear_rowwise(qx, qw, sx, sw, out_kind=OUT_BF16, out=None, accum=ACC_EXACT):
+    """y[m, n] = acc * fp32(sx[m] * sw[n]) with acc = sum_k dec(qx) dec(qw);
+    qx [..., K] E4M3 with per-row scales sx [...] (FP32), qw [N, K] with
+    per-channel scales sw [N].  out_kind OUT_BF16 or OUT_F32."""
+    _need(qx, "qx", torch.uint8)
+    dev = qx.device
+    _need(qw, "qw", torch.uint8, dev)
+    K = qx.shape[-1]
+    N = qw.shape[0]
+    if qw.dim() != 2 or qw.shape[1] != K:
+        raise ValueError("qw must be [N, K] with qx [..., K]")
+    M = math.prod(qx.shape[:-1])
+    _need(sx, "sx", torch.float32, dev)
+    _need(sw, "sw", torch.float32, dev)
+    if sx.numel() != M or sw.numel() != N:
+        raise ValueError("sx must hold one scale per row of qx and sw one per row of qw")
+    dtype = {OUT_BF16: torch.bfloat16, OUT_F32: torch.float32}.get(out_kind)
+    if dtype is None:
+        raise ValueError("out_kind must be OUT_BF16 or OUT_F32")
+    if out is None:
+        out = torch.empty((*qx.shape[:-1], N), dtype=dtype, device=dev)
+    _need(out, "out", dtype, dev)
+    if out.numel() != M * N:
+        raise ValueError("out must hold M * N elements")
+    _lib.call("fp8_linear_rowwise", _ptr(qx), _ptr(qw), _ptr(out), M, N, K,
+              _ptr(sx), _ptr(sw), out_kind, accum, _stream(qx))
+    return out
+
+
 def silu_mul_2in_fp8(g, u, s_out, out=None, alpha=None, beta=None):
     """E4M3 codes of g * sigmoid(alpha g) * (u + beta) at ``s_out``; g and u
     BF16 of equal shape.  Without alpha and beta this is plain SwiGLU

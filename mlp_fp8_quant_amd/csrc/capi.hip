@@ -136,6 +136,34 @@ int fp8_linear(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
   return hip_status(launch_gemm(qx, qw, y, M, N, K, d_sx, d_sw, out_kind, d_sy, accum, cus, stream));
 }
 
+int fp8_linear_rowwise(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
+                       int64_t N, int64_t K, const float* d_sx, const float* d_sw,
+                       int out_kind, int accum, hipStream_t stream) {
+  if (out_kind == FP8MOT_OUT_FP8) return FP8MOT_ERR_UNSUPPORTED;
+  int st = check_linear(qx, qw, y, M, N, K, d_sx, d_sw, out_kind, nullptr, accum);
+  if (st != FP8MOT_OK || M == 0 || N == 0) return st;
+  if (!aligned16(d_sx) || !aligned16(d_sw)) return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  // out kinds 3 / 4 of the launcher: BF16 / FP32 with per-row scales
+  const int kind = out_kind == FP8MOT_OUT_BF16 ? 3 : 4;
+  return hip_status(launch_gemm(qx, qw, y, M, N, K, d_sx, d_sw, kind, nullptr, accum, cus, stream));
+}
+
+int fp8_quant_per_row(const uint16_t* x, uint8_t* q, float* d_scales,
+                      int64_t rows, int64_t K, hipStream_t stream) {
+  if (rows < 0 || K < 0 || (K % 16) != 0) return FP8MOT_ERR_INVALID_ARG;
+  if (rows > 0 && K > INT64_MAX / rows) return FP8MOT_ERR_INVALID_ARG;
+  if (rows == 0 || K == 0) return FP8MOT_OK;
+  if (x == nullptr || q == nullptr || d_scales == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(q)) return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_quant_per_row(x, q, d_scales, rows, K, ew_blocks(cus), stream));
+}
+
 int silu_mul_2in_fp8_ab(const uint16_t* g, const uint16_t* u, uint8_t* q,
                         int64_t n, const float* d_s_out, float alpha, float beta,
                         hipStream_t stream) {

@@ -165,6 +165,92 @@ __global__ __launch_bounds__(kThreads) void silu_mul_adj_scalar_kernel(
   }
 }
 
+// Per-token (per-row) dynamic quantization (model card "Cosmos3-Nano-Policy-
+// DROID, FP8 + RTN + moving-average activation observer", section 3.2:
+// per-channel weights, per-token activations).  One workgroup per row of K
+// elements (K % 16 == 0).  The row's amax is the integer max of
+// (bits & 0x7FFF) -- exact, and NaN patterns sort above Inf; scale =
+// fp32(amax) / 448; q = e4m3(x / s) with one IEEE division per element.  A
+// zero row (s = 0) keeps its signed zeros; a NaN row gets a NaN scale and
+// all-NaN codes.  UH > 0: the row stays in registers between the amax and
+// the quantization (up to UH 16-element units per thread); UH == 0: the row
+// is read twice (the second time from cache).
+template <int UH>
+__global__ __launch_bounds__(kThreads) void quant_per_row_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+    float* __restrict__ scales, int64_t rows, int64_t K) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t units = K >> 4;                 // 16-element units per row
+  auto max16 = [](uint32_t m, const u32x4 a, const u32x4 b) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+      m = m > lo ? m : lo;
+      m = m > hi ? m : hi;
+    }
+    return m;
+  };
+  auto encode16 = [](const u32x4 a, const u32x4 b, float s) {
+    float f[16];
+    unpack8(a, f);
+    unpack8(b, f + 8);
+    if (s != 0.0f) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) f[j] = f[j] / s;   // IEEE division
+    }
+    u32x4 o;
+    o.x = e4m3_pack4(f[0], f[1], f[2], f[3]);
+    o.y = e4m3_pack4(f[4], f[5], f[6], f[7]);
+    o.z = e4m3_pack4(f[8], f[9], f[10], f[11]);
+    o.w = e4m3_pack4(f[12], f[13], f[14], f[15]);
+    return o;
+  };
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + r * K);
+    u32x4* qr = reinterpret_cast<u32x4*>(q + r * K);
+    uint32_t m = 0;
+    u32x4 hold[UH > 0 ? UH : 1][2];
+    if constexpr (UH > 0) {
+#pragma unroll
+      for (int k = 0; k < UH; ++k) {
+        const int64_t i = threadIdx.x + k * kThreads;
+        if (i < units) {
+          hold[k][0] = __builtin_nontemporal_load(xr + 2 * i);
+          hold[k][1] = __builtin_nontemporal_load(xr + 2 * i + 1);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < UH; ++k)
+        if (threadIdx.x + k * kThreads < units) m = max16(m, hold[k][0], hold[k][1]);
+    } else {
+      for (int64_t i = threadIdx.x; i < units; i += kThreads) m = max16(m, xr[2 * i], xr[2 * i + 1]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t o = __shfl_xor(m, off, 64);
+      m = m > o ? m : o;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) m = m > red[w] ? m : red[w];
+    const float s = __uint_as_float(m << 16) / 448.0f;
+    if (threadIdx.x == 0) scales[r] = s;
+    if constexpr (UH > 0) {
+#pragma unroll
+      for (int k = 0; k < UH; ++k) {
+        const int64_t i = threadIdx.x + k * kThreads;
+        if (i < units) __builtin_nontemporal_store(encode16(hold[k][0], hold[k][1], s), qr + i);
+      }
+    } else {
+      for (int64_t i = threadIdx.x; i < units; i += kThreads)
+        qr[i] = encode16(xr[2 * i], xr[2 * i + 1], s);
+    }
+    __syncthreads();   // red is reused by the next row
+  }
+}
+
 // Block-wide max of non-negative FP32 bit patterns (integer order == value
 // order for non-negative floats; NaN patterns sort above +Inf) into the
 // state's pending slot.  Only a block that can raise the running value
@@ -309,6 +395,22 @@ hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                                hipStream_t stream) {
   hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(n >> 6, 2 * max_blocks)),
                      dim3(kThreads), 0, stream, x, q, n, d_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_per_row(const uint16_t* x, uint8_t* q, float* scales,
+                                int64_t rows, int64_t K, int max_blocks,
+                                hipStream_t stream) {
+  const int64_t b = rows < 2 * (int64_t)max_blocks ? rows : 2 * (int64_t)max_blocks;
+  const dim3 grid((unsigned)(b > 0 ? b : 1)), block(kThreads);
+  const int64_t units = K >> 4;
+  // keep the row in registers when it fits 2 or 8 units per thread
+  if (units <= 2 * kThreads)
+    hipLaunchKernelGGL(quant_per_row_kernel<2>, grid, block, 0, stream, x, q, scales, rows, K);
+  else if (units <= 8 * kThreads)
+    hipLaunchKernelGGL(quant_per_row_kernel<8>, grid, block, 0, stream, x, q, scales, rows, K);
+  else
+    hipLaunchKernelGGL(quant_per_row_kernel<0>, grid, block, 0, stream, x, q, scales, rows, K);
   return hipGetLastError();
 }
 

@@ -213,8 +213,8 @@ struct GemmArgs {
   const uint8_t* B2;  // fused: the up weight [N, K]
   void* C;            // [M, N]   (fused: the FP8 SwiGLU output)
   int M, N, K;
-  const float* sx;
-  const float* sw;    // (fused: gate weight scale)
+  const float* sx;    // (OUT 3, 4: per-row scales [M])
+  const float* sw;    // (fused: gate weight scale; OUT 3, 4: per-channel scales [N])
   const float* sw2;   // fused: up weight scale
   const float* sy;    // FP8 output scale (fused: the down projection's input scale)
   int tiles_m, tiles_n;
@@ -222,7 +222,8 @@ struct GemmArgs {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// OUT: 0 BF16, 1 FP8, 2 FP32.  FUSED: gate and up GEMMs of a gated MLP in one
+// OUT: 0 BF16, 1 FP8, 2 FP32 with per-tensor scales; 3 BF16, 4 FP32 with a
+// scale per row of A and per row of B (per-token / per-channel).  FUSED: gate and up GEMMs of a gated MLP in one
 // tile (BN = 256 = 128 gate rows + 128 up rows of the same output columns)
 // whose epilogue applies SwiGLU and writes FP8, bit for bit what the separate
 // BF16 GEMMs followed by silu_mul_2in_fp8 produce.
@@ -455,9 +456,24 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   // four lanes of a quad hold four consecutive columns.  A 4x4 transpose
   // inside the quad (two DPP exchanges) turns that into one row-piece of four
   // consecutive columns per lane, stored straight to global memory.
-  const float alpha = __fmul_rn(*g.sx, *g.sw);
+  // Per-row scales (OUT 3, 4): alpha[m, n] = fp32(s_x[m] * s_w[n]), formed
+  // per output exactly as the per-tensor alpha is; the four consecutive rows
+  // of a register group take one 16-byte load of s_x, each column one s_w.
+  constexpr bool ROWWISE = OUT >= 3;
+  const float alpha = ROWWISE ? 0.0f : __fmul_rn(*g.sx, *g.sw);
+  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(g.sx + (ROWWISE ? m0 : 0), ROWWISE ? (int64_t)(M - m0) * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(g.sw + (ROWWISE ? n0 : 0), ROWWISE ? (int64_t)(N - n0) * 4 : 0);
+  auto row_scales4 = [&](int row) -> v4i {   // s_x of tile rows row .. row + 3 (row % 4 == 0)
+    return __builtin_amdgcn_raw_buffer_load_b128(rsx, row * 4, 0, 0);
+  };
+  float swc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    swc[j] = ROWWISE ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                           rsw, (wn * WTN + (lane & 31) + j * 32) * 4, 0, 0))
+                     : 0.0f;
   void* __restrict__ C = g.C;
-  constexpr int ESZ = OUT == 0 ? 2 : (OUT == 1 ? 1 : 4);
+  constexpr int ESZ = (OUT == 0 || OUT == 3) ? 2 : (OUT == 1 ? 1 : 4);
   const __amdgpu_buffer_rsrc_t rc_rs =
       make_rsrc(static_cast<uint8_t*>(C) + ((int64_t)m0 * N) * ESZ, (int64_t)(M - m0) * N * ESZ);
   const int col_l = wn * WTN + (lane & 31);          // + j*32
@@ -495,7 +511,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
           const int off = (m0 + row < M && col < N) ? row * N + col : kOOB;
           __builtin_amdgcn_raw_buffer_store_b32(w, rq_rs, off, 0, 0);
         }
-  } else if constexpr (OUT == 0) {
+  } else if constexpr (OUT == 0 || OUT == 3) {
     // BF16: four rows of a column -> two packed dwords, transposed in the
     // quad so that each lane stores four consecutive columns of one row
     // (8 bytes).  Rows whose width is not a multiple of 4 take 2-byte stores.
@@ -504,11 +520,17 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int q = 0; q < 4; ++q) {
+        v4i sxr = {0, 0, 0, 0};
+        if constexpr (ROWWISE) sxr = row_scales4(row_l + i * 32 + q * 8);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t a = bf16x2_rne(__fmul_rn(acc[i][j][4 * q + 0], alpha), __fmul_rn(acc[i][j][4 * q + 1], alpha));
-          const uint32_t b = bf16x2_rne(__fmul_rn(acc[i][j][4 * q + 2], alpha), __fmul_rn(acc[i][j][4 * q + 3], alpha));
+        for (int j = 0; j < FN; ++j) {
+          float al[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            al[e] = ROWWISE ? __fmul_rn(__int_as_float(sxr[e]), swc[j]) : alpha;
+          const uint32_t a = bf16x2_rne(__fmul_rn(acc[i][j][4 * q + 0], al[0]), __fmul_rn(acc[i][j][4 * q + 1], al[1]));
+          const uint32_t b = bf16x2_rne(__fmul_rn(acc[i][j][4 * q + 2], al[2]), __fmul_rn(acc[i][j][4 * q + 3], al[3]));
           uint32_t d0, d1;
           quad_transpose_halves(a, b, qt, d0, d1);
           const int row = row_l + i * 32 + q * 8 + qt;
@@ -525,23 +547,31 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
             }
           }
         }
+      }
   } else {
     const float sy = (OUT == 1) ? *g.sy : 1.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = col_l + j * 32;
+      for (int q = 0; q < 4; ++q) {
+        v4i sxr = {0, 0, 0, 0};
+        if constexpr (ROWWISE) sxr = row_scales4(row_l + i * 32 + q * 8);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = row_l + i * 32 + (v >> 2) * 8 + (v & 3);
-          const bool ok = (m0 + row < M) && (n0 + col < N);
-          const int off = ok ? (row * N + n0 + col) * ESZ : kOOB;
-          const float y = __fmul_rn(acc[i][j][v], alpha);
-          if constexpr (OUT == 1)
-            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e4m3_encode(y / sy), rc_rs, off, 0, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rc_rs, off, 0, 0);
+        for (int j = 0; j < FN; ++j) {
+          const int col = col_l + j * 32;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * q + e;
+            const int row = row_l + i * 32 + q * 8 + e;
+            const bool ok = (m0 + row < M) && (n0 + col < N);
+            const int off = ok ? (row * N + n0 + col) * ESZ : kOOB;
+            const float al = ROWWISE ? __fmul_rn(__int_as_float(sxr[e]), swc[j]) : alpha;
+            const float y = __fmul_rn(acc[i][j][v], al);
+            if constexpr (OUT == 1)
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e4m3_encode(y / sy), rc_rs, off, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rc_rs, off, 0, 0);
+          }
         }
       }
   }
@@ -558,6 +588,12 @@ hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
       break;
     case 1:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false>), grid, block, 0, stream, a);
+      break;
+    case 3:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 3, ENGINE, false>), grid, block, 0, stream, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 4, ENGINE, false>), grid, block, 0, stream, a);
       break;
     default:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false>), grid, block, 0, stream, a);
@@ -579,7 +615,7 @@ hipError_t launch_fused(GemmArgs a, hipStream_t stream) {
 // still gives about one workgroup per CU.  Measured on the workload shapes:
 // 256x256 tiles with 8 waves (two per SIMD) are fastest once there are
 // ~0.7 tiles per CU; below that 256x128 (8 waves) and then 128x128 (4 waves)
-// keep the CUs busy.  FP8MOT_GEMM_CFG=<n> forces one configuration (tuning).
+// keep the CUs busy.  FP8MOT_GEMM_CFG=<1|5|3> forces one configuration (tuning).
 template <int ENGINE>
 hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stream) {
   auto tiles = [&](int bm, int bn) {
@@ -595,9 +631,7 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
     cfg = tiles(256, 256) >= want ? 1 : (tiles(256, 128) >= want ? 5 : 3);
   }
   switch (cfg) {
-    case 0: return launch_tiled<256, 256, 2, 2, ENGINE>(a, out_kind, stream);
     case 1: return launch_tiled<256, 256, 2, 4, ENGINE>(a, out_kind, stream);
-    case 4: return launch_tiled<256, 256, 4, 2, ENGINE>(a, out_kind, stream);
     case 5: return launch_tiled<256, 128, 4, 2, ENGINE>(a, out_kind, stream);
     default: return launch_tiled<128, 128, 2, 2, ENGINE>(a, out_kind, stream);
   }

@@ -20,6 +20,12 @@ hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                                const float* d_scale, int max_blocks,
                                hipStream_t stream);
 
+// Per-row dynamic quantization of x [rows, K] (K % 16 == 0): scales[r] =
+// amax(row r) / 448, q[r, :] = e4m3(x[r, :] / scales[r]).
+hipError_t launch_quant_per_row(const uint16_t* x, uint8_t* q, float* scales,
+                                int64_t rows, int64_t K, int max_blocks,
+                                hipStream_t stream);
+
 // q = e4m3(g * sigmoid(alpha g) * (u + beta) / s); (1, 0) is plain SwiGLU.
 hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
                            int64_t n, const float* d_s, float alpha, float beta,
@@ -41,6 +47,8 @@ hipError_t launch_scale_from_state(const fp8mot_observer_state_dev* st,
 
 // FP8 GEMM y[M,N] = (qa[M,K] . qb[N,K]^T) * (sx*sw), out_kind per fp8mot_out,
 // accum per fp8mot_acc (0: F16 MFMA on exactly decoded codes, 1: FP8 MFMA).
+// out_kind 3 (BF16) and 4 (FP32): sx [M] and sw [N] are per-row scales and
+// y[m,n] = acc * fp32(sx[m] * sw[n]).
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        int64_t M, int64_t N, int64_t K, const float* sx,
                        const float* sw, int out_kind, const float* sy,

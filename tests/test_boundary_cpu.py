@@ -31,7 +31,8 @@ def test_header_declares_the_hot_path_calls():
     for n in ("fp8_quant_static", "fp8_linear", "silu_mul_2in_fp8",
               "gated_mlp_fp8", "qkv_fp8", "fp8_observe", "fp8_scale_from_state",
               "fp8_check_shared_scale", "fp8_gate_up_swiglu",
-              "silu_mul_2in_fp8_ab", "silu_mul_fp8"):
+              "silu_mul_2in_fp8_ab", "silu_mul_fp8", "fp8_quant_per_row",
+              "fp8_linear_rowwise"):
         assert n in names
 
 
@@ -146,3 +147,26 @@ def test_swiglu_variant_refusals_before_any_device_access():
     assert lib.silu_mul_2in_fp8_ab(fake, odd, fake, 16, s, 1.0, 0.0, null) == 2
     assert lib.silu_mul_fp8(odd, fake, 2, 16, s, 1.0, 0.0, null) == 2
     assert lib.silu_mul_fp8(fake, odd, 2, 16, s, 1.0, 0.0, null) == 2
+
+
+def test_rowwise_refusals_before_any_device_access():
+    lib = _lib()
+    P = ctypes.c_void_p
+    fake = P(0x10000)        # never dereferenced: every case below is refused
+    odd = P(0x10001)
+    null = P(0)
+    s = fake
+    # per-row quantize: K % 16, negative sizes, NULL scales, alignment
+    assert lib.fp8_quant_per_row(fake, fake, fake, 4, 24, null) == 1
+    assert lib.fp8_quant_per_row(fake, fake, fake, -1, 16, null) == 1
+    assert lib.fp8_quant_per_row(fake, fake, null, 4, 16, null) == 1
+    assert lib.fp8_quant_per_row(odd, fake, fake, 4, 16, null) == 2
+    assert lib.fp8_quant_per_row(null, null, null, 0, 16, null) == 0
+    # per-row GEMM: FP8 output unsupported, NULL scales, bad enums, alignment
+    assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, s, s, 1, 0, null) == 4
+    assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, null, s, 0, 0, null) == 4
+    assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 24, s, s, 0, 0, null) == 1
+    assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, s, s, 0, 7, null) == 1
+    assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, s, s, 5, 0, null) == 1
+    assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, odd, s, 0, 0, null) == 2
+    assert lib.fp8_linear_rowwise(null, null, null, 0, 4, 16, s, s, 0, 0, null) == 0

@@ -1,0 +1,138 @@
+"""GPU parity: per-row FP8 -- per-token activation quantization, per-channel
+weight RTN and the GEMM with a scale per row of each operand (model card
+"Cosmos3-Nano-Policy-DROID, FP8 + RTN + moving-average activation observer",
+section 3.2)."""
+
+import numpy as np
+import pytest
+import torch
+
+import mlp_fp8_quant_amd as fp8
+from mlp_fp8_quant_amd import workloads
+from oracle.formats import bf16_ulps, f32_to_bf16
+from oracle.linear import gemm_exact
+from oracle.rowwise import (epilogue_rowwise_alpha, epilogue_rowwise_f32,
+                            quant_per_row)
+
+from gpu_util import (check_gemm_fp8_engine, device, fp8_mfma_group_bound,
+                      host_bits, host_f32, host_u8, to_dev_bf16, to_dev_u8)
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(rng, rows, K, lo=1e-3, hi=1e3):
+    x = rng.standard_normal((rows, K)).astype(np.float32)
+    x *= rng.uniform(lo, hi, (rows, 1)).astype(np.float32)
+    return workloads.to_bf16_bits(x)
+
+
+def _quant_dev(x, dev):
+    q, s = fp8.fp8_quant_per_row(to_dev_bf16(x.ravel(), dev).view(x.shape))
+    return host_u8(q), host_f32(s)
+
+
+@pytest.mark.parametrize("rows,K", [(1, 16), (17, 2048), (300, 5120), (64, 25600), (3, 48), (5, 32784)])
+def test_quant_per_row_bitexact(rows, K):
+    dev = device()
+    x = _rows(np.random.default_rng(rows * 7 + K), rows, K)
+    q, s = _quant_dev(x, dev)
+    wq, ws = quant_per_row(x)
+    assert np.array_equal(s.view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(q, wq)
+
+
+def test_quant_per_row_special_rows_and_rank3():
+    dev = device()
+    rows = np.zeros((6, 32), np.float32)
+    rows[1] = np.linspace(-3, 3, 32)
+    rows[1, 5] = np.nan
+    rows[2] = np.linspace(-1, 1, 32)
+    rows[2, 7] = np.inf
+    rows[3] = np.linspace(-448, 448, 32)
+    rows[4] = 1e-30                    # tiny: its own scale brings it to 448
+    rows[5, ::2] = -0.0
+    x = workloads.to_bf16_bits(rows)
+    x[0, 1::2] = 0x8000                # -0 in the zero row
+    q, s = _quant_dev(x, dev)
+    wq, ws = quant_per_row(x)
+    assert np.array_equal(q, wq)
+    assert np.array_equal(np.isnan(s), np.isnan(ws)) and np.array_equal(s[~np.isnan(s)], ws[~np.isnan(ws)])
+    assert s[0] == 0 and s[5] == 0 and q[0, 1] == 0x80
+    # rank 3: [2, 3, K] quantizes as 6 rows
+    x3 = _rows(np.random.default_rng(5), 6, 64).reshape(2, 3, 64)
+    q3, s3 = fp8.fp8_quant_per_row(to_dev_bf16(x3.ravel(), dev).view(2, 3, 64))
+    assert q3.shape == (2, 3, 64) and s3.shape == (2, 3)
+    wq3, ws3 = quant_per_row(x3.reshape(6, 64))
+    assert np.array_equal(host_u8(q3).reshape(6, 64), wq3)
+    assert np.array_equal(host_f32(s3).ravel(), ws3)
+
+
+def _check_rowwise_f32(y32, S, A, alpha):
+    a = alpha.astype(np.float64)
+    err = np.abs(y32.astype(np.float64) - a * S)
+    bad = err > 1e-5 * a * A
+    assert not bad.any(), f"{bad.sum()} outputs exceed 1e-5*sum|terms|"
+
+
+def _check_rowwise_bf16(yb, y32, S, A, alpha):
+    ref32 = (S.astype(np.float32) * alpha).astype(np.float32)
+    d = bf16_ulps(yb, f32_to_bf16(ref32))
+    idx = d > 1
+    if idx.any():   # the FP32 output passes 1e-5 and the BF16 output is its RNE
+        a = alpha.astype(np.float64)
+        ok32 = np.abs(y32[idx].astype(np.float64) - a[idx] * S[idx]) <= 1e-5 * a[idx] * A[idx]
+        assert (ok32 & (f32_to_bf16(y32[idx]) == yb[idx])).all()
+
+
+@pytest.mark.parametrize("engine", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (37, 129, 144), (300, 200, 4096), (257, 385, 1040)])
+def test_linear_rowwise_against_oracle(engine, M, N, K):
+    dev = device()
+    rng = np.random.default_rng(M + N + K + engine)
+    x = _rows(rng, M, K, 0.05, 20)
+    w = _rows(rng, N, K, 0.002, 0.05)
+    qx_d, sx_d = fp8.fp8_quant_per_row(to_dev_bf16(x.ravel(), dev).view(M, K))
+    qw_d, sw_d = fp8.fp8_quant_per_row(to_dev_bf16(w.ravel(), dev).view(N, K))
+    qx, sx = quant_per_row(x)
+    qw, sw = quant_per_row(w)
+    assert np.array_equal(host_u8(qx_d), qx) and np.array_equal(host_u8(qw_d), qw)
+    S, A = gemm_exact(qx, qw)
+    alpha = epilogue_rowwise_alpha(sx, sw)
+    y32 = host_f32(fp8.fp8_linear_rowwise(qx_d, qw_d, sx_d, sw_d, out_kind=fp8.OUT_F32, accum=engine))
+    yb = host_bits(fp8.fp8_linear_rowwise(qx_d, qw_d, sx_d, sw_d, accum=engine))
+    if engine == fp8.ACC_EXACT:
+        _check_rowwise_f32(y32, S, A, alpha)
+        _check_rowwise_bf16(yb, y32, S, A, alpha)
+    else:
+        check_gemm_fp8_engine(y32, S, A, alpha, fp8_mfma_group_bound(qx, qw))
+        assert np.array_equal(yb, f32_to_bf16(y32))
+
+
+def test_linear_rowwise_gen_mlp_shape_sampled_rows():
+    # gate projection of the gen-tower MLP: M = 2048 tokens, N = 8192, K = 2048
+    dev = device()
+    rng = np.random.default_rng(77)
+    M, N, K = 2048, 8192, 2048
+    x = _rows(rng, M, K, 0.1, 10)
+    w = workloads.to_bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.02))
+    qx_d, sx_d = fp8.fp8_quant_per_row(to_dev_bf16(x.ravel(), dev).view(M, K))
+    qw_d, sw_d = fp8.fp8_quant_per_row(to_dev_bf16(w.ravel(), dev).view(N, K))
+    y32 = host_f32(fp8.fp8_linear_rowwise(qx_d, qw_d, sx_d, sw_d, out_kind=fp8.OUT_F32))
+    rows = np.sort(rng.choice(M, 48, replace=False))
+    qx, sx = quant_per_row(x[rows])
+    qw, sw = quant_per_row(w)
+    assert np.array_equal(host_u8(qx_d)[rows], qx)
+    S, A = gemm_exact(qx, qw)
+    _check_rowwise_f32(y32[rows], S, A, epilogue_rowwise_alpha(sx, sw))
+
+
+def test_rowwise_refusals():
+    dev = device()
+    q = torch.zeros((4, 32), dtype=torch.uint8, device=dev)
+    s4 = torch.ones(4, dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        fp8.fp8_linear_rowwise(q, q, s4, s4, out_kind=fp8.OUT_FP8)
+    with pytest.raises(ValueError):
+        fp8.fp8_linear_rowwise(q, q, s4[:3], s4)
+    with pytest.raises(fp8.Fp8motError):
+        fp8.fp8_quant_per_row(torch.zeros((4, 24), dtype=torch.bfloat16, device=dev))
