@@ -199,6 +199,7 @@ def main():
 
     large = None if args.no_large else elementwise_large(fp8, torch, dev, stream)
     rowwise = None if args.no_large else per_row_fp8(fp8, torch, dev, stream, M, H, I)
+    topology = None if args.no_large else fused_topology(fp8, torch, dev, stream, qx, sx, sh, q, s)
 
     if args.copy_calib_mb > 0:
         n = args.copy_calib_mb << 20
@@ -223,9 +224,70 @@ def main():
         "fp8_mfma_engine": fp8_engine,
         "elementwise_large": large,
         "per_row_fp8": rowwise,
+        "fused_topology": topology,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out))
+
+
+def fused_topology(fp8, torch, dev, stream, qx, sx, sh, q, s):
+    """The topology the split path replaces, timed beside it (pull request
+    "Load static FP8 Cosmos3 Nano/Super checkpoints without re-quantizing
+    them": split GEMMs cost the same as fused ones, the fused group loses each
+    member's own scale).  Gated MLP at the bench workload: the split path's
+    fused gate/up + SwiGLU kernel; the fused topology (gate and up
+    re-quantized onto max(s), one [M, 2I] GEMM, one-input SwiGLU); and the two
+    split GEMMs written into column slices of one [M, 2I] buffer (row stride
+    2I) + one-input SwiGLU.  Split Q/K/V [3072, 4096] x 3 * [4096, 4096]
+    against one [3072, 12288] GEMM.  Also the share of codes the
+    re-quantization changed (gate and up)."""
+    def timed(f, reps=20):
+        for _ in range(2):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {}
+    M, I = qx.shape[0], q["gate"].shape[0]
+    group = torch.cat([s["gate"], s["up"]])
+    rg = fp8.fp8_requantize_onto_max(q["gate"], s["gate"], group)
+    ru = fp8.fp8_requantize_onto_max(q["up"], s["up"], group)
+    smax = torch.max(group).reshape(1)
+    wf = torch.cat([rg, ru])
+    out["requantized_codes_changed"] = {
+        "gate": float((rg != q["gate"]).float().mean()), "up": float((ru != q["up"]).float().mean()),
+        "scale_ratio": float(torch.min(group) / torch.max(group))}
+    qh = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    y2 = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    out["split_fused_kernel_us"] = timed(lambda: fp8.fp8_gate_up_swiglu(
+        qx, q["gate"], sx, s["gate"], q["up"], s["up"], sh, out=qh))
+    out["fused_topology_us"] = timed(lambda: (fp8.fp8_linear(qx, wf, sx, smax, out=y2),
+                                              fp8.silu_mul_fp8(y2, sh, out=qh)))
+    out["split_into_slices_us"] = timed(lambda: (
+        fp8.fp8_linear_into(qx, q["gate"], sx, s["gate"], y2, col0=0),
+        fp8.fp8_linear_into(qx, q["up"], sx, s["up"], y2, col0=I),
+        fp8.silu_mul_fp8(y2, sh, out=qh)))
+    del y2, rg, ru, wf
+    # split vs fused Q/K/V at the split-QKV workload shape
+    Mq, Hq = 3072, 4096
+    qa = torch.randint(0, 0x7E, (Mq, Hq), dtype=torch.uint8, device=dev)
+    ws = [torch.randint(0, 0x7E, (Hq, Hq), dtype=torch.uint8, device=dev) for _ in range(3)]
+    sc = torch.tensor([1e-3], device=dev)
+    ys = [torch.empty((Mq, Hq), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    wcat = torch.cat(ws)
+    ycat = torch.empty((Mq, 3 * Hq), dtype=torch.bfloat16, device=dev)
+    out["qkv_split_3_gemms_us"] = timed(lambda: [fp8.fp8_linear(qa, w, sc, sc, out=y) for w, y in zip(ws, ys)])
+    out["qkv_fused_1_gemm_us"] = timed(lambda: fp8.fp8_linear(qa, wcat, sc, sc, out=ycat))
+    del qa, ws, ys, wcat, ycat
+    torch.cuda.empty_cache()
+    return out
 
 
 def per_row_fp8(fp8, torch, dev, stream, M, H, I):

@@ -217,6 +217,33 @@ int fp8_linear_rowwise(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
                        int out_kind, int accum, hipStream_t stream);
 
 /* ------------------------------------------------------------------ */
+/* Fused-topology comparison (what the split path avoids)              */
+/* ------------------------------------------------------------------ */
+
+/* fp8_linear writing into a row-strided output: row m of y starts ldc
+ * elements after row m - 1 (ldc >= N), so two projections can write the
+ * column slices [:, 0:N) and [:, N:2N) of one [M, 2N] buffer ([PR] "What
+ * changed": writing both GEMMs into column slices of one buffer went wrong
+ * in the original stack because the GEMM assumed the leading dimension was
+ * N).  Elements of y outside [0, M) x [0, N) are not written.  ldc < N is
+ * FP8MOT_ERR_INVALID_ARG; other arguments as fp8_linear. */
+int fp8_linear_ldc(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
+                   int64_t N, int64_t K, int64_t ldc, const float* d_sx,
+                   const float* d_sw, int out_kind, const float* d_sy, int accum,
+                   hipStream_t stream);
+
+/* The failure mode of a fused group that keeps one scale ([PR]
+ * "Description": each member re-quantized as FP8-round((s_i * qW_i) /
+ * max(s))), for the fused-topology comparison only:
+ *   out[k] = e4m3(fp32(fp32(*d_s_member * dec(qw[k])) / max(d_s_group[0..g-1])))
+ * qw, out: E4M3 [n], 16-byte aligned; d_s_member: FP32 scalar, d_s_group:
+ * FP32 [group_size] (1..64), device memory.  NULL scales are
+ * FP8MOT_ERR_UNSUPPORTED. */
+int fp8_requantize_onto_max(const uint8_t* qw, uint8_t* out, int64_t n,
+                            const float* d_s_member, const float* d_s_group,
+                            int group_size, hipStream_t stream);
+
+/* ------------------------------------------------------------------ */
 /* Composites (one shared quantization, contiguous outputs, no sync)   */
 /* ------------------------------------------------------------------ */
 

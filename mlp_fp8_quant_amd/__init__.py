@@ -10,7 +10,8 @@ from .api import (ACC_EXACT, ACC_FP8_MFMA, OBS_MAX,  # noqa: F401
                   OBS_MOVING_AVG, OUT_BF16, OUT_F32,
                   OUT_FP8, Fp8motError, debug_quant_launches,
                   fp8_check_shared_scale, fp8_gate_up_swiglu, fp8_linear,
-                  fp8_linear_rowwise, fp8_quant_per_row,
+                  fp8_linear_into, fp8_linear_rowwise, fp8_quant_per_row,
+                  fp8_requantize_onto_max,
                   fp8_observe,
                   fp8_observe_swiglu, fp8_quant_static, fp8_scale_from_state,
                   gated_mlp_fp8, gated_mlp_fp8_workspace, init,

@@ -26,6 +26,10 @@ SIGNATURES = {
     "fp8_quant_per_row": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p]),
     "fp8_linear_rowwise": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64,
                                    c_void_p, c_void_p, c_int, c_int, c_void_p]),
+    "fp8_linear_ldc": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64,
+                               c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p]),
+    "fp8_requantize_onto_max": (c_int, [c_void_p, c_void_p, c_i64, c_void_p, c_void_p,
+                                        c_int, c_void_p]),
     "silu_mul_2in_fp8": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_void_p,
                                  c_void_p]),
     "silu_mul_2in_fp8_ab": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_void_p,

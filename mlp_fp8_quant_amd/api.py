@@ -149,6 +149,52 @@ def fp8_linear_rowwise(qx, qw, sx, sw, out_kind=OUT_BF16, out=None, accum=ACC_EX
     return out
 
 
+def fp8_linear_into(qx, qw, sx, sw, out, col0=0, out_kind=OUT_BF16, sy=None,
+                    accum=ACC_EXACT):
+    """fp8_linear writing into columns [col0, col0 + N) of an existing
+    row-major output ``out`` [..., L] (L >= col0 + N): the row stride of the
+    written block is L.  Nothing outside that column block is touched."""
+    _need(qx, "qx", torch.uint8)
+    dev = qx.device
+    _need(qw, "qw", torch.uint8, dev)
+    K = qx.shape[-1]
+    N = qw.shape[0]
+    if qw.dim() != 2 or qw.shape[1] != K:
+        raise ValueError("qw must be [N, K] with qx [..., K]")
+    M = math.prod(qx.shape[:-1])
+    _scale(sx, "sx", dev)
+    _scale(sw, "sw", dev)
+    dtype = {OUT_BF16: torch.bfloat16, OUT_FP8: torch.uint8, OUT_F32: torch.float32}[out_kind]
+    _need(out, "out", dtype, dev)
+    L = out.shape[-1]
+    if out.numel() != M * L or col0 < 0 or col0 + N > L:
+        raise ValueError("out must be [..., L] with M rows and col0 + N <= L")
+    if out_kind == OUT_FP8:
+        _scale(sy, "sy", dev)
+    base = out.data_ptr() + col0 * out.element_size()
+    _lib.call("fp8_linear_ldc", _ptr(qx), _ptr(qw), ctypes.c_void_p(base), M, N, K, L,
+              _ptr(sx), _ptr(sw), out_kind, _ptr(sy) if sy is not None else None,
+              accum, _stream(qx))
+    return out
+
+
+def fp8_requantize_onto_max(qw, s_member, s_group, out=None):
+    """Codes of qw re-quantized onto the largest scale of its group (the fused
+    single-scale failure mode; comparison workloads only)."""
+    _need(qw, "qw", torch.uint8)
+    dev = qw.device
+    _scale(s_member, "s_member", dev)
+    _need(s_group, "s_group", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(qw)
+    _need(out, "out", torch.uint8, dev)
+    if out.numel() != qw.numel():
+        raise ValueError("out must match qw")
+    _lib.call("fp8_requantize_onto_max", _ptr(qw), _ptr(out), qw.numel(), _ptr(s_member),
+              _ptr(s_group), s_group.numel(), _stream(qw))
+    return out
+
+
 def silu_mul_2in_fp8(g, u, s_out, out=None, alpha=None, beta=None):
     """E4M3 codes of g * sigmoid(alpha g) * (u + beta) at ``s_out``; g and u
     BF16 of equal shape.  Without alpha and beta this is plain SwiGLU

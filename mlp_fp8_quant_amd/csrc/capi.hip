@@ -151,6 +151,37 @@ int fp8_linear_rowwise(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
   return hip_status(launch_gemm(qx, qw, y, M, N, K, d_sx, d_sw, kind, nullptr, accum, cus, stream));
 }
 
+int fp8_linear_ldc(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
+                   int64_t N, int64_t K, int64_t ldc, const float* d_sx,
+                   const float* d_sw, int out_kind, const float* d_sy, int accum,
+                   hipStream_t stream) {
+  int st = check_linear(qx, qw, y, M, N, K, d_sx, d_sw, out_kind, d_sy, accum);
+  if (st != FP8MOT_OK) return st;
+  if (ldc < N || ldc > INT32_MAX) return FP8MOT_ERR_INVALID_ARG;
+  if (M > 0 && ldc > INT64_MAX / M) return FP8MOT_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FP8MOT_OK;
+  int cus = 0;
+  st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_gemm(qx, qw, y, M, N, K, d_sx, d_sw, out_kind, d_sy, accum, cus,
+                                stream, ldc));
+}
+
+int fp8_requantize_onto_max(const uint8_t* qw, uint8_t* out, int64_t n,
+                            const float* d_s_member, const float* d_s_group,
+                            int group_size, hipStream_t stream) {
+  if (d_s_member == nullptr || d_s_group == nullptr) return FP8MOT_ERR_UNSUPPORTED;
+  if (n < 0 || group_size < 1 || group_size > 64) return FP8MOT_ERR_INVALID_ARG;
+  if (n == 0) return FP8MOT_OK;
+  if (qw == nullptr || out == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(qw) || !aligned16(out)) return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_requant_onto_max(qw, out, n, d_s_member, d_s_group, group_size,
+                                            ew_blocks(cus), stream));
+}
+
 int fp8_quant_per_row(const uint16_t* x, uint8_t* q, float* d_scales,
                       int64_t rows, int64_t K, hipStream_t stream) {
   if (rows < 0 || K < 0 || (K % 16) != 0) return FP8MOT_ERR_INVALID_ARG;

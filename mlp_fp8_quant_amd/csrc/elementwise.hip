@@ -251,6 +251,48 @@ __global__ __launch_bounds__(kThreads) void quant_per_row_kernel(
   }
 }
 
+// Re-quantization onto the group's largest scale: what a fused projection
+// that keeps one scale does to each member (pull request "Load static FP8
+// Cosmos3 Nano/Super checkpoints without re-quantizing them", "Description":
+// FP8-round((s_i * qW_i) / max(s)) instead of keeping s_i * qW_i).  Kept to
+// build the fused-topology comparison; the split path never calls it.
+// out = e4m3(fp32(fp32(s_i * dec(q)) / s_max)), decode by the hardware FP8 ->
+// FP32 conversion (exact; NaN codes give NaN).  16 codes per thread per step.
+__global__ __launch_bounds__(kThreads) void requant_onto_max_kernel(
+    const uint8_t* __restrict__ q, uint8_t* __restrict__ out, int64_t n,
+    const float* __restrict__ s_i, const float* __restrict__ s_group, int group) {
+  const float si = *s_i;
+  float smax = s_group[0];
+  for (int k = 1; k < group; ++k) smax = smax > s_group[k] ? smax : s_group[k];
+  const int64_t units = n >> 4;
+  const u32x4* qv = reinterpret_cast<const u32x4*>(q);
+  u32x4* ov = reinterpret_cast<u32x4*>(out);
+  auto requant4 = [&](uint32_t w) -> uint32_t {
+    float f[4];
+    f[0] = __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    f[1] = __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    f[2] = __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    f[3] = __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = __fmul_rn(si, f[j]) / smax;
+    return e4m3_pack4(f[0], f[1], f[2], f[3]);
+  };
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < units;
+       i += (int64_t)gridDim.x * kThreads) {
+    const u32x4 v = qv[i];
+    u32x4 o;
+    o.x = requant4(v.x);
+    o.y = requant4(v.y);
+    o.z = requant4(v.z);
+    o.w = requant4(v.w);
+    ov[i] = o;
+  }
+  if (blockIdx.x == 0) {
+    const int64_t t = (units << 4) + threadIdx.x;
+    if (t < n) out[t] = (uint8_t)(requant4(q[t]) & 0xFFu);
+  }
+}
+
 // Block-wide max of non-negative FP32 bit patterns (integer order == value
 // order for non-negative floats; NaN patterns sort above +Inf) into the
 // state's pending slot.  Only a block that can raise the running value
@@ -411,6 +453,14 @@ hipError_t launch_quant_per_row(const uint16_t* x, uint8_t* q, float* scales,
     hipLaunchKernelGGL(quant_per_row_kernel<8>, grid, block, 0, stream, x, q, scales, rows, K);
   else
     hipLaunchKernelGGL(quant_per_row_kernel<0>, grid, block, 0, stream, x, q, scales, rows, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_requant_onto_max(const uint8_t* q, uint8_t* out, int64_t n,
+                                   const float* s_i, const float* s_group, int group,
+                                   int max_blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(requant_onto_max_kernel, dim3(grid_for(n >> 4, max_blocks)),
+                     dim3(kThreads), 0, stream, q, out, n, s_i, s_group, group);
   return hipGetLastError();
 }
 

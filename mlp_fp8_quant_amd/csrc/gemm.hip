@@ -218,6 +218,7 @@ struct GemmArgs {
   const float* sw2;   // fused: up weight scale
   const float* sy;    // FP8 output scale (fused: the down projection's input scale)
   int tiles_m, tiles_n;
+  int ldc;            // row stride of C in elements (>= N; N for a contiguous C)
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -473,9 +474,10 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
                            rsw, (wn * WTN + (lane & 31) + j * 32) * 4, 0, 0))
                      : 0.0f;
   void* __restrict__ C = g.C;
+  const int ldc = g.ldc;
   constexpr int ESZ = (OUT == 0 || OUT == 3) ? 2 : (OUT == 1 ? 1 : 4);
   const __amdgpu_buffer_rsrc_t rc_rs =
-      make_rsrc(static_cast<uint8_t*>(C) + ((int64_t)m0 * N) * ESZ, (int64_t)(M - m0) * N * ESZ);
+      make_rsrc(static_cast<uint8_t*>(C) + ((int64_t)m0 * ldc) * ESZ, (int64_t)(M - m0) * ldc * ESZ);
   const int col_l = wn * WTN + (lane & 31);          // + j*32
   const int row_l = wm * WTM + (lane >> 5) * 4;       // + i*32 + 8*(v/4) + v%4
   const int qt = lane & 3;                            // lane's place in its quad
@@ -489,7 +491,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
     const float alpha_u = __fmul_rn(*g.sx, *g.sw2);
     const float rs = 1.0f / *g.sy;
     const __amdgpu_buffer_rsrc_t rq_rs =
-        make_rsrc(static_cast<uint8_t*>(C) + (int64_t)m0 * N, (int64_t)(M - m0) * N);
+        make_rsrc(static_cast<uint8_t*>(C) + (int64_t)m0 * ldc, (int64_t)(M - m0) * ldc);
     const int col_q = n0 + (wn * WTN) / 2 + ((lane & 31) & ~3);   // + p*32
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -508,14 +510,14 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
           const uint32_t w = quad_transpose_bytes(e4m3_pack4(h[0], h[1], h[2], h[3]), qt);
           const int row = row_l + i * 32 + q * 8 + qt;       // row within tile
           const int col = col_q + p * 32;
-          const int off = (m0 + row < M && col < N) ? row * N + col : kOOB;
+          const int off = (m0 + row < M && col < N) ? row * ldc + col : kOOB;
           __builtin_amdgcn_raw_buffer_store_b32(w, rq_rs, off, 0, 0);
         }
   } else if constexpr (OUT == 0 || OUT == 3) {
     // BF16: four rows of a column -> two packed dwords, transposed in the
     // quad so that each lane stores four consecutive columns of one row
     // (8 bytes).  Rows whose width is not a multiple of 4 take 2-byte stores.
-    const bool vec_ok = (N % 4) == 0;
+    const bool vec_ok = (N % 4) == 0 && (ldc % 4) == 0;
     const int col_q = n0 + wn * WTN + ((lane & 31) & ~3);   // + j*32
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -536,12 +538,12 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
           const int row = row_l + i * 32 + q * 8 + qt;
           const int col = col_q + j * 32;
           if (vec_ok) {
-            const int off = (m0 + row < M && col < N) ? (row * N + col) * 2 : kOOB;
+            const int off = (m0 + row < M && col < N) ? (row * ldc + col) * 2 : kOOB;
             __builtin_amdgcn_raw_buffer_store_b64((v2u){d0, d1}, rc_rs, off, 0, 0);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int off = (m0 + row < M && col + e < N) ? (row * N + col + e) * 2 : kOOB;
+              const int off = (m0 + row < M && col + e < N) ? (row * ldc + col + e) * 2 : kOOB;
               const uint32_t d = e < 2 ? d0 : d1;
               __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(d >> ((e & 1) * 16)), rc_rs, off, 0, 0);
             }
@@ -564,7 +566,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
             const int v = 4 * q + e;
             const int row = row_l + i * 32 + q * 8 + e;
             const bool ok = (m0 + row < M) && (n0 + col < N);
-            const int off = ok ? (row * N + n0 + col) * ESZ : kOOB;
+            const int off = ok ? (row * ldc + n0 + col) * ESZ : kOOB;
             const float al = ROWWISE ? __fmul_rn(__int_as_float(sxr[e]), swc[j]) : alpha;
             const float y = __fmul_rn(acc[i][j][v], al);
             if constexpr (OUT == 1)
@@ -642,8 +644,9 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        int64_t M, int64_t N, int64_t K, const float* sx,
                        const float* sw, int out_kind, const float* sy,
-                       int accum, int num_cus, hipStream_t stream) {
-  GemmArgs a{qa, qb, nullptr, y, (int)M, (int)N, (int)K, sx, sw, nullptr, sy, 0, 0};
+                       int accum, int num_cus, hipStream_t stream, int64_t ldc) {
+  GemmArgs a{qa, qb, nullptr, y, (int)M, (int)N, (int)K, sx, sw, nullptr, sy, 0, 0,
+             (int)(ldc > 0 ? ldc : N)};
   if (accum == 1) return launch_engine<1>(a, out_kind, num_cus, stream);
   return launch_engine<0>(a, out_kind, num_cus, stream);
 }
@@ -652,7 +655,7 @@ hipError_t launch_gemm_swiglu(const uint8_t* qx, const uint8_t* wg, const uint8_
                               uint8_t* qh, int64_t M, int64_t I, int64_t H,
                               const float* sx, const float* sg, const float* su,
                               const float* sh, int accum, hipStream_t stream) {
-  GemmArgs a{qx, wg, wu, qh, (int)M, (int)I, (int)H, sx, sg, su, sh, 0, 0};
+  GemmArgs a{qx, wg, wu, qh, (int)M, (int)I, (int)H, sx, sg, su, sh, 0, 0, (int)I};
   if (accum == 1) return launch_fused<256, 2, 4, 1>(a, stream);
   return launch_fused<256, 2, 4, 0>(a, stream);
 }

@@ -49,10 +49,18 @@ hipError_t launch_scale_from_state(const fp8mot_observer_state_dev* st,
 // accum per fp8mot_acc (0: F16 MFMA on exactly decoded codes, 1: FP8 MFMA).
 // out_kind 3 (BF16) and 4 (FP32): sx [M] and sw [N] are per-row scales and
 // y[m,n] = acc * fp32(sx[m] * sw[n]).
+// ldc: row stride of y in elements (0: N, a contiguous y).
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        int64_t M, int64_t N, int64_t K, const float* sx,
                        const float* sw, int out_kind, const float* sy,
-                       int accum, int num_cus, hipStream_t stream);
+                       int accum, int num_cus, hipStream_t stream, int64_t ldc = 0);
+
+// Re-quantization of a fused group's member onto the group's largest scale
+// (the failure mode of a single-scale fused group):
+// out = e4m3(fp32(fp32(s_i * dec(q)) / max(s_group[0..group-1]))).
+hipError_t launch_requant_onto_max(const uint8_t* q, uint8_t* out, int64_t n,
+                                   const float* s_i, const float* s_group, int group,
+                                   int max_blocks, hipStream_t stream);
 
 // Gate and up GEMMs of a gated MLP with the SwiGLU-FP8 epilogue in one launch:
 // qh[M,I] = e4m3(silu(bf16(G)) * bf16(U) / sh) with G = qx.wg^T * (sx*sg),

@@ -32,7 +32,7 @@ def test_header_declares_the_hot_path_calls():
               "gated_mlp_fp8", "qkv_fp8", "fp8_observe", "fp8_scale_from_state",
               "fp8_check_shared_scale", "fp8_gate_up_swiglu",
               "silu_mul_2in_fp8_ab", "silu_mul_fp8", "fp8_quant_per_row",
-              "fp8_linear_rowwise"):
+              "fp8_linear_rowwise", "fp8_linear_ldc", "fp8_requantize_onto_max"):
         assert n in names
 
 
@@ -170,3 +170,25 @@ def test_rowwise_refusals_before_any_device_access():
     assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, s, s, 5, 0, null) == 1
     assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, odd, s, 0, 0, null) == 2
     assert lib.fp8_linear_rowwise(null, null, null, 0, 4, 16, s, s, 0, 0, null) == 0
+
+
+def test_fused_topology_refusals_before_any_device_access():
+    lib = _lib()
+    P = ctypes.c_void_p
+    fake = P(0x10000)        # never dereferenced: every case below is refused
+    odd = P(0x10001)
+    null = P(0)
+    s = fake
+    # ldc below N, K % 16, NULL scales, alignment
+    assert lib.fp8_linear_ldc(fake, fake, fake, 4, 32, 16, 31, s, s, 0, null, 0, null) == 1
+    assert lib.fp8_linear_ldc(fake, fake, fake, 4, 32, 24, 64, s, s, 0, null, 0, null) == 1
+    assert lib.fp8_linear_ldc(fake, fake, fake, 4, 32, 16, 64, null, s, 0, null, 0, null) == 4
+    assert lib.fp8_linear_ldc(fake, fake, odd, 4, 32, 16, 64, s, s, 0, null, 0, null) == 2
+    assert lib.fp8_linear_ldc(null, null, null, 0, 32, 16, 64, s, s, 0, null, 0, null) == 0
+    # requantize: NULL scales, bad group size, alignment, empty
+    assert lib.fp8_requantize_onto_max(fake, fake, 16, null, s, 2, null) == 4
+    assert lib.fp8_requantize_onto_max(fake, fake, 16, s, null, 2, null) == 4
+    assert lib.fp8_requantize_onto_max(fake, fake, 16, s, s, 0, null) == 1
+    assert lib.fp8_requantize_onto_max(fake, fake, -1, s, s, 2, null) == 1
+    assert lib.fp8_requantize_onto_max(odd, fake, 16, s, s, 2, null) == 2
+    assert lib.fp8_requantize_onto_max(null, null, 0, s, s, 2, null) == 0
