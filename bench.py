@@ -285,7 +285,13 @@ def fused_topology(fp8, torch, dev, stream, qx, sx, sh, q, s):
     ycat = torch.empty((Mq, 3 * Hq), dtype=torch.bfloat16, device=dev)
     out["qkv_split_3_gemms_us"] = timed(lambda: [fp8.fp8_linear(qa, w, sc, sc, out=y) for w, y in zip(ws, ys)])
     out["qkv_fused_1_gemm_us"] = timed(lambda: fp8.fp8_linear(qa, wcat, sc, sc, out=ycat))
-    del qa, ws, ys, wcat, ycat
+    # the split path as shipped: qkv_fp8 (quantize once + one grouped launch)
+    xq = torch.randn((Mq, Hq), device=dev).to(torch.bfloat16)
+    wsq = torch.empty(fp8.qkv_fp8_workspace(Mq, Hq), dtype=torch.uint8, device=dev)
+    out["qkv_fp8_composite_us"] = timed(lambda: fp8.qkv_fp8(xq, sc, ws[0], sc, ws[1], sc, ws[2], sc,
+                                                            outs=ys, workspace=wsq))
+    out["qkv_quantize_us"] = timed(lambda: fp8.fp8_quant_static(xq, sc, out=wsq[:Mq * Hq].view(Mq, Hq)))
+    del qa, ws, ys, wcat, ycat, xq, wsq
     torch.cuda.empty_cache()
     return out
 

@@ -290,6 +290,8 @@ size_t qkv_fp8_workspace(int64_t M, int64_t H);
  *   qX = quant(x; sx); yq = linear(qX, wq; sx, sq); yk = ...; yv = ...
  * x: [M, H]; wq: [Nq, H]; wk: [Nk, H]; wv: [Nv, H]; yq: [M, Nq], yk: [M, Nk],
  * yv: [M, Nv], three separate contiguous BF16 tensors.  H multiple of 16.
+ * The three GEMMs run as one grouped launch (bitwise what three fp8_linear
+ * calls give).  A member with N == 0 is skipped and its pointers may be NULL.
  * Cross-attention, where k/v read a different tensor than q, must not use
  * this call: quantize each input separately and use fp8_linear.  `accum`
  * selects the GEMM engine (fp8mot_acc). */

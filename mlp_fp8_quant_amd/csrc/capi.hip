@@ -306,9 +306,11 @@ int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
   if (M > INT32_MAX || H > INT32_MAX || Nq > INT32_MAX || Nk > INT32_MAX || Nv > INT32_MAX)
     return FP8MOT_ERR_INVALID_ARG;
   if (M == 0) return FP8MOT_OK;
-  if (!x || !wq || !wk || !wv || !yq || !yk || !yv) return FP8MOT_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(wq) || !aligned16(wk) || !aligned16(wv) ||
-      !aligned16(yq) || !aligned16(yk) || !aligned16(yv))
+  // a member with N == 0 has nothing to read or write (its pointers may be NULL)
+  if (!x || (Nq > 0 && (!wq || !yq)) || (Nk > 0 && (!wk || !yk)) || (Nv > 0 && (!wv || !yv)))
+    return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(x) || (Nq > 0 && (!aligned16(wq) || !aligned16(yq))) ||
+      (Nk > 0 && (!aligned16(wk) || !aligned16(yk))) || (Nv > 0 && (!aligned16(wv) || !aligned16(yv))))
     return FP8MOT_ERR_MISALIGNED;
   if (ws == nullptr || !aligned256(ws) || ws_bytes < qkv_fp8_workspace(M, H))
     return FP8MOT_ERR_WORKSPACE;
@@ -321,12 +323,27 @@ int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
     g_quant_launches.fetch_add(1);
     e = launch_quant_static(x, qx, M * H, d_sx, ew_blocks(cus), stream);
   }
-  if (e == hipSuccess && Nq > 0)
-    e = launch_gemm(qx, wq, yq, M, Nq, H, d_sx, d_sq, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
-  if (e == hipSuccess && Nk > 0)
-    e = launch_gemm(qx, wk, yk, M, Nk, H, d_sx, d_sk, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
-  if (e == hipSuccess && Nv > 0)
-    e = launch_gemm(qx, wv, yv, M, Nv, H, d_sx, d_sv, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
+  // the three projections in one grouped launch (the non-empty ones): tiles
+  // of all three share qX rows in L2 and fill the machine together
+  const uint8_t* wb[3];
+  void* yb[3];
+  const float* sb[3];
+  int64_t nb[3];
+  int groups = 0;
+  const uint8_t* w3[3] = {wq, wk, wv};
+  uint16_t* y3[3] = {yq, yk, yv};
+  const float* s3[3] = {d_sq, d_sk, d_sv};
+  const int64_t n3[3] = {Nq, Nk, Nv};
+  for (int p = 0; p < 3; ++p) {
+    if (n3[p] == 0) continue;
+    wb[groups] = w3[p];
+    yb[groups] = y3[p];
+    sb[groups] = s3[p];
+    nb[groups] = n3[p];
+    ++groups;
+  }
+  if (e == hipSuccess && groups > 0)
+    e = launch_gemm_grouped(qx, groups, wb, yb, nb, M, H, d_sx, sb, accum, cus, stream);
   return hip_status(e);
 }
 

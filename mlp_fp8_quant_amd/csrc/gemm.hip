@@ -219,6 +219,15 @@ struct GemmArgs {
   const float* sy;    // FP8 output scale (fused: the down projection's input scale)
   int tiles_m, tiles_n;
   int ldc;            // row stride of C in elements (>= N; N for a contiguous C)
+  // Grouped launch (groups > 1): up to three projections of the same A, each
+  // with its own B, C, weight scale and N (contiguous C), in one grid; the
+  // tile columns of group p follow those of groups 0 .. p-1.
+  int groups;
+  const uint8_t* gB[3];
+  void* gC[3];
+  const float* gsw[3];
+  int gN[3];
+  int gtiles_n[3];
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -230,7 +239,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // BF16 GEMMs followed by silu_mul_2in_fp8 produce.
 template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
-  const int M = g.M, N = g.N, K = g.K;
+  const int M = g.M, K = g.K;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
@@ -248,12 +257,29 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   const int wm = wave / WN, wn = wave % WN;
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  // this tile's projection (a grouped launch walks the groups' tile columns)
+  const uint8_t* gB = g.B;
+  void* gCp = g.C;
+  const float* gsw = g.sw;
+  int N = g.N, ldc = g.ldc;
+  if (g.groups > 1) {
+    int p = 0;
+    while (p + 1 < g.groups && tn >= g.gtiles_n[p]) {
+      tn -= g.gtiles_n[p];
+      ++p;
+    }
+    gB = g.gB[p];
+    gCp = g.gC[p];
+    gsw = g.gsw[p];
+    N = g.gN[p];
+    ldc = N;
+  }
   // output columns of this tile start at n0 (fused: 128 of each of G and U)
   const int m0 = tm * BM, n0 = tn * (FUSED ? BN / 2 : BN);
 
   // operand windows start at the tile's first row; rows past M (N) read as 0
   const v4i ra_rs = make_rsrc_words(g.A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
-  const v4i rb_rs = make_rsrc_words(g.B + (int64_t)n0 * K, (int64_t)(N - n0) * K);
+  const v4i rb_rs = make_rsrc_words(gB + (int64_t)n0 * K, (int64_t)(N - n0) * K);
   const v4i rb2_rs = FUSED ? make_rsrc_words(g.B2 + (int64_t)n0 * K, (int64_t)(N - n0) * K) : rb_rs;
 
   // Copy q (= wave * LPW + i) of a stage fills LDS rows q*RPI .. q*RPI+RPI-1
@@ -410,7 +436,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   // have the epilogue's kernel arguments in registers before the loop, so no
   // scalar load is still pending inside it (that would turn every LDS wait
   // there into a wait for all LDS reads)
-  asm volatile("" ::"s"(g.sx), "s"(g.sw), "s"(g.sw2), "s"(g.sy), "s"(g.C));
+  asm volatile("" ::"s"(g.sx), "s"(gsw), "s"(g.sw2), "s"(g.sy), "s"(gCp));
 #pragma unroll
   for (int u = 0; u < NB; ++u)
     if (u < KT) issue_stage(u, u);
@@ -461,9 +487,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   // per output exactly as the per-tensor alpha is; the four consecutive rows
   // of a register group take one 16-byte load of s_x, each column one s_w.
   constexpr bool ROWWISE = OUT >= 3;
-  const float alpha = ROWWISE ? 0.0f : __fmul_rn(*g.sx, *g.sw);
+  const float alpha = ROWWISE ? 0.0f : __fmul_rn(*g.sx, *gsw);
   const __amdgpu_buffer_rsrc_t rsx = make_rsrc(g.sx + (ROWWISE ? m0 : 0), ROWWISE ? (int64_t)(M - m0) * 4 : 0);
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(g.sw + (ROWWISE ? n0 : 0), ROWWISE ? (int64_t)(N - n0) * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(gsw + (ROWWISE ? n0 : 0), ROWWISE ? (int64_t)(N - n0) * 4 : 0);
   auto row_scales4 = [&](int row) -> v4i {   // s_x of tile rows row .. row + 3 (row % 4 == 0)
     return __builtin_amdgcn_raw_buffer_load_b128(rsx, row * 4, 0, 0);
   };
@@ -473,8 +499,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
     swc[j] = ROWWISE ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
                            rsw, (wn * WTN + (lane & 31) + j * 32) * 4, 0, 0))
                      : 0.0f;
-  void* __restrict__ C = g.C;
-  const int ldc = g.ldc;
+  void* __restrict__ C = gCp;
   constexpr int ESZ = (OUT == 0 || OUT == 3) ? 2 : (OUT == 1 ? 1 : 4);
   const __amdgpu_buffer_rsrc_t rc_rs =
       make_rsrc(static_cast<uint8_t*>(C) + ((int64_t)m0 * ldc) * ESZ, (int64_t)(M - m0) * ldc * ESZ);
@@ -582,7 +607,15 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
 template <int BM, int BN, int WM, int WN, int ENGINE>
 hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
   a.tiles_m = (a.M + BM - 1) / BM;
-  a.tiles_n = (a.N + BN - 1) / BN;
+  if (a.groups > 1) {
+    a.tiles_n = 0;
+    for (int p = 0; p < a.groups; ++p) {
+      a.gtiles_n[p] = (a.gN[p] + BN - 1) / BN;
+      a.tiles_n += a.gtiles_n[p];
+    }
+  } else {
+    a.tiles_n = (a.N + BN - 1) / BN;
+  }
   const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
   switch (out_kind) {
     case 0:
@@ -621,7 +654,13 @@ hipError_t launch_fused(GemmArgs a, hipStream_t stream) {
 template <int ENGINE>
 hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stream) {
   auto tiles = [&](int bm, int bn) {
-    return (int64_t)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    int64_t tn = 0;
+    if (a.groups > 1) {
+      for (int p = 0; p < a.groups; ++p) tn += (a.gN[p] + bn - 1) / bn;
+    } else {
+      tn = (a.N + bn - 1) / bn;
+    }
+    return (int64_t)((a.M + bm - 1) / bm) * tn;
   };
   static const int forced = [] {
     const char* e = getenv("FP8MOT_GEMM_CFG");
@@ -645,17 +684,46 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        int64_t M, int64_t N, int64_t K, const float* sx,
                        const float* sw, int out_kind, const float* sy,
                        int accum, int num_cus, hipStream_t stream, int64_t ldc) {
-  GemmArgs a{qa, qb, nullptr, y, (int)M, (int)N, (int)K, sx, sw, nullptr, sy, 0, 0,
-             (int)(ldc > 0 ? ldc : N)};
+  GemmArgs a{};
+  a.A = qa; a.B = qb; a.C = y;
+  a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  a.sx = sx; a.sw = sw; a.sy = sy;
+  a.ldc = (int)(ldc > 0 ? ldc : N);
+  a.groups = 1;
   if (accum == 1) return launch_engine<1>(a, out_kind, num_cus, stream);
   return launch_engine<0>(a, out_kind, num_cus, stream);
+}
+
+hipError_t launch_gemm_grouped(const uint8_t* qa, int groups, const uint8_t* const* qb,
+                               void* const* y, const int64_t* N, int64_t M, int64_t K,
+                               const float* sx, const float* const* sw, int accum,
+                               int num_cus, hipStream_t stream) {
+  GemmArgs a{};
+  a.A = qa;
+  a.M = (int)M; a.K = (int)K;
+  a.sx = sx;
+  a.groups = groups;
+  for (int p = 0; p < groups; ++p) {
+    a.gB[p] = qb[p];
+    a.gC[p] = y[p];
+    a.gsw[p] = sw[p];
+    a.gN[p] = (int)N[p];
+  }
+  a.B = qb[0]; a.C = y[0]; a.sw = sw[0]; a.N = (int)N[0]; a.ldc = (int)N[0];
+  if (accum == 1) return launch_engine<1>(a, 0, num_cus, stream);
+  return launch_engine<0>(a, 0, num_cus, stream);
 }
 
 hipError_t launch_gemm_swiglu(const uint8_t* qx, const uint8_t* wg, const uint8_t* wu,
                               uint8_t* qh, int64_t M, int64_t I, int64_t H,
                               const float* sx, const float* sg, const float* su,
                               const float* sh, int accum, hipStream_t stream) {
-  GemmArgs a{qx, wg, wu, qh, (int)M, (int)I, (int)H, sx, sg, su, sh, 0, 0, (int)I};
+  GemmArgs a{};
+  a.A = qx; a.B = wg; a.B2 = wu; a.C = qh;
+  a.M = (int)M; a.N = (int)I; a.K = (int)H;
+  a.sx = sx; a.sw = sg; a.sw2 = su; a.sy = sh;
+  a.ldc = (int)I;
+  a.groups = 1;
   if (accum == 1) return launch_fused<256, 2, 4, 1>(a, stream);
   return launch_fused<256, 2, 4, 0>(a, stream);
 }

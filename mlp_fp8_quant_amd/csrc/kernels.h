@@ -55,6 +55,14 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        const float* sw, int out_kind, const float* sy,
                        int accum, int num_cus, hipStream_t stream, int64_t ldc = 0);
 
+// Up to three BF16-output GEMMs of the same A in one launch (split Q/K/V):
+// y[p] [M, N[p]] = (qa . qb[p]^T) * (sx * sw[p]); groups with N[p] == 0 must
+// be left out by the caller.
+hipError_t launch_gemm_grouped(const uint8_t* qa, int groups, const uint8_t* const* qb,
+                               void* const* y, const int64_t* N, int64_t M, int64_t K,
+                               const float* sx, const float* const* sw, int accum,
+                               int num_cus, hipStream_t stream);
+
 // Re-quantization of a fused group's member onto the group's largest scale
 // (the failure mode of a single-scale fused group):
 // out = e4m3(fp32(fp32(s_i * dec(q)) / max(s_group[0..group-1]))).

@@ -259,3 +259,27 @@ def test_gate_up_swiglu_ragged_equals_parts(accum, M, I, H):
     G = fp8.fp8_linear(qx, dg, dsx, dsg, accum=accum)
     U = fp8.fp8_linear(qx, du, dsx, dsu, accum=accum)
     assert torch.equal(qh, fp8.silu_mul_2in_fp8(G, U, dsh))
+
+
+@pytest.mark.parametrize("ns", [(384, 128, 96), (4096, 1024, 1024), (200, 0, 72)])
+@pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+def test_qkv_grouped_launch_equals_separate_gemms(ns, accum):
+    # qkv_fp8 runs the projections as one grouped launch; with unequal N
+    # (GQA-like) and an empty member it still equals three separate
+    # fp8_linear calls bit for bit
+    dev = device()
+    rng = np.random.default_rng(sum(ns) + accum)
+    M, H = 300, 512
+    x = workloads.to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    dx = to_dev_bf16(x.ravel(), dev).view(M, H)
+    sx = scalar(0.01, dev)
+    ws, ss = [], []
+    for n in ns:
+        ws.append(to_dev_u8(rng.integers(0, 0x7E, (n, H), dtype=np.uint8), dev))
+        ss.append(scalar(0.001 * (1 + len(ss)), dev))
+    yq, yk, yv = fp8.qkv_fp8(dx, sx, ws[0], ss[0], ws[1], ss[1], ws[2], ss[2], accum=accum)
+    qx = fp8.fp8_quant_static(dx, sx)
+    for y, w, s in zip((yq, yk, yv), ws, ss):
+        assert y.shape == (M, w.shape[0])
+        if w.shape[0]:
+            assert torch.equal(y, fp8.fp8_linear(qx, w, sx, s, accum=accum))
