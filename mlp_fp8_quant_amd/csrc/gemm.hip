@@ -25,13 +25,13 @@
 // Tiling (both engines):
 //  * a workgroup computes a BM x BN tile with WM x WN waves, each wave a
 //    (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks;
-//  * operands are K-contiguous ([M,K] and [N,K]); a stage holds 64 K of the
-//    tile's A and B rows (64 LDS bytes per row), four stages live in LDS and
-//    the buffer unit copies them from memory straight into LDS, three stages
+//  * operands are K-contiguous ([M,K] and [N,K]); a stage holds 128 K of the
+//    tile's A and B rows (128 LDS bytes per row), two stages live in LDS and
+//    the buffer unit copies them from memory straight into LDS, one stage
 //    ahead of the MFMAs, one barrier per stage (details below);
-//  * the 16-byte chunk c of LDS row r lives at chunk c ^ ((r >> 2) & 3): the
+//  * the 16-byte chunk c of LDS row r lives at chunk c ^ ((r >> 1) & 7): the
 //    LDS serves a 128-bit access 16 lanes at a time across 64 four-byte
-//    banks (256 bytes = four rows), and 16 consecutive rows of one logical
+//    banks (256 bytes = two rows), and 16 consecutive rows of one logical
 //    chunk then cover all 16 distinct 16-byte bank groups;
 //  * an MFMA operand fragment is read per lane as whole 16-byte chunks: lane
 //    l takes row l % 32 and K positions (l / 32) * w .. + w of the MFMA's K
@@ -183,19 +183,21 @@ __device__ __forceinline__ void quad_transpose_halves(uint32_t a, uint32_t b, in
   }
 }
 
-// Operand staging: a stage covers KS = 64 of K.  Its LDS rows hold the 64
-// FP8 codes of one A or B row (A rows first, then B rows), and NB = 4 stages
+// Operand staging: a stage covers KS = 128 of K.  Its LDS rows hold the 128
+// FP8 codes of one A or B row (A rows first, then B rows), and NB = 2 stages
 // live in LDS at once.  The global -> LDS copy is done by the buffer unit
 // itself (buffer_load_dwordx4 with the LDS flag): one wave-wide instruction
-// fills 1 KB of a stage -- lane i's 16 bytes land at byte 16*i -- with no
-// registers in between and no wait in the wave.  Loads that fall outside a
-// buffer resource write zeros, which pads ragged M, N and K.  The copies of
-// stage s + NB go out as soon as every wave has finished reading stage s,
-// spread between the MFMAs of that step, so three stages are always in
-// flight.  (Measured on MI355X: staging through registers and ds_write, or
-// 3 or 5 stages, is no faster.)
-constexpr int KS = 64;            // K per stage
-constexpr int NB = 4;             // stages resident in LDS
+// fills 1 KB of a stage (8 rows) -- lane i's 16 bytes land at byte 16*i --
+// with no registers in between and no wait in the wave.  Loads that fall
+// outside a buffer resource write zeros, which pads ragged M, N and K.  The
+// copies of stage s + 2 go out as soon as every wave has finished reading
+// stage s, spread between the MFMAs of that step.  Measured on MI355X: whole
+// 128-byte row segments per copy move L2-resident data ~1.8x faster than
+// 64-byte ones (the L2 serves a request per segment), which outweighs the
+// deeper prefetch that 64-K stages (four in LDS) allow; staging through
+// registers and ds_write was no faster.
+constexpr int KS = 128;           // K per stage
+constexpr int NB = 2;             // stages resident in LDS
 constexpr int CH = KS / 16;       // 16-byte chunks per LDS row
 constexpr int RW = 256 / KS;      // LDS rows per 256-byte bank window
 constexpr int RPI = 1024 / KS;    // LDS rows filled by one wave-wide copy
@@ -367,6 +369,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   // are issued one after each 32-row block of A (the rest after the last),
   // so that the address unit is fed steadily instead of every wave queueing
   // its copies at once.
+  constexpr int CPR = (LPW + FM - 1) / FM;   // copies issued after each block row
   auto mf = [&](int slot, auto copies, int cb, int cs) {
     constexpr bool kCopies = decltype(copies)::value;
     if constexpr (ENGINE == 0) {
@@ -394,7 +397,11 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[i], b0[j], acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[i], b1[j], acc[i][j], 0, 0, 0);
         }
-        if constexpr (kCopies) { if (i < LPW) issue_copy(cb, cs, i); }
+        if constexpr (kCopies) {
+#pragma unroll
+          for (int c = 0; c < CPR; ++c)
+            if (i * CPR + c < LPW) issue_copy(cb, cs, i * CPR + c);
+        }
       }
     } else {
 #pragma unroll
@@ -403,13 +410,14 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               fa[slot][i], fb[slot][j], acc[i][j], 0, 0, 0, 0, 0, 0);
-        if constexpr (kCopies) { if (i < LPW) issue_copy(cb, cs, i); }
+        if constexpr (kCopies) {
+#pragma unroll
+          for (int c = 0; c < CPR; ++c)
+            if (i * CPR + c < LPW) issue_copy(cb, cs, i * CPR + c);
+        }
       }
     }
-    if constexpr (kCopies) {
-#pragma unroll
-      for (int r = FM; r < LPW; ++r) issue_copy(cb, cs, r);
-    }
+
   };
   // wait until at most n of this wave's stage copies are still in flight
   // (s_waitcnt vmcnt(n), expcnt and lgkmcnt left alone: gfx9 encoding)
