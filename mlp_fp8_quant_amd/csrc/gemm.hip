@@ -184,20 +184,20 @@ __device__ __forceinline__ void quad_transpose_halves(uint32_t a, uint32_t b, in
 }
 
 // Operand staging: a stage covers KS = 128 of K.  Its LDS rows hold the 128
-// FP8 codes of one A or B row (A rows first, then B rows), and NB = 2 stages
-// live in LDS at once.  The global -> LDS copy is done by the buffer unit
-// itself (buffer_load_dwordx4 with the LDS flag): one wave-wide instruction
-// fills 1 KB of a stage (8 rows) -- lane i's 16 bytes land at byte 16*i --
-// with no registers in between and no wait in the wave.  Loads that fall
-// outside a buffer resource write zeros, which pads ragged M, N and K.  The
-// copies of stage s + 2 go out as soon as every wave has finished reading
-// stage s, spread between the MFMAs of that step.  Measured on MI355X: whole
-// 128-byte row segments per copy move L2-resident data ~1.8x faster than
-// 64-byte ones (the L2 serves a request per segment), which outweighs the
-// deeper prefetch that 64-K stages (four in LDS) allow; staging through
-// registers and ds_write was no faster.
+// FP8 codes of one A or B row (A rows first, then B rows), and NB stages
+// live in LDS at once (two, or with DEEP as many as fit, up to four).  The
+// global -> LDS copy is done by the buffer unit itself (buffer_load_dwordx4
+// with the LDS flag): one wave-wide instruction fills 1 KB of a stage (8
+// rows) -- lane i's 16 bytes land at byte 16*i -- with no registers in
+// between and no wait in the wave.  Loads that fall outside a buffer resource
+// write zeros, which pads ragged M, N and K.  The copies of stage s + NB go
+// out as soon as every wave has finished reading stage s, spread between the
+// MFMAs of that step.  Measured on MI355X: whole 128-byte row segments per
+// copy move L2-resident data ~1.8x faster than 64-byte ones (the L2 serves a
+// request per segment), which outweighs the deeper prefetch that 64-K stages
+// allow in the same LDS; staging through registers and ds_write was no
+// faster.
 constexpr int KS = 128;           // K per stage
-constexpr int NB = 2;             // stages resident in LDS
 constexpr int CH = KS / 16;       // 16-byte chunks per LDS row
 constexpr int RW = 256 / KS;      // LDS rows per 256-byte bank window
 constexpr int RPI = 1024 / KS;    // LDS rows filled by one wave-wide copy
@@ -239,13 +239,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // tile (BN = 256 = 128 gate rows + 128 up rows of the same output columns)
 // whose epilogue applies SwiGLU and writes FP8, bit for bit what the separate
 // BF16 GEMMs followed by silu_mul_2in_fp8 produce.
-template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED>
+template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED, bool DEEP = false>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   const int M = g.M, K = g.K;
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
   constexpr int STAGE = (BM + BN) * KS;
+  // stages resident in LDS: two, or with DEEP as many as the 160 KB hold, up
+  // to four (two for 256x256 tiles, three for 256x128, four for 128x128)
+  constexpr int NB = !DEEP ? 2 : (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;
   constexpr int A_INS = BM / RPI, INS = (BM + BN) / RPI;   // wave-wide copies per stage
   constexpr int LPW = INS / NW;                            // ... per wave
   static_assert(LPW * NW == INS, "tile rows / waves");
@@ -612,8 +615,33 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int ENGINE>
+template <int BM, int BN, int WM, int WN, int ENGINE, bool DEEP>
 hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
+  const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+  switch (out_kind) {
+    case 0:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      break;
+    case 1:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      break;
+    case 3:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 3, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 4, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+// Tile counts of a launch with BM x BN tiles (a grouped launch adds up the
+// groups' tile columns).
+template <int BM, int BN>
+void set_tiles(GemmArgs& a) {
   a.tiles_m = (a.M + BM - 1) / BM;
   if (a.groups > 1) {
     a.tiles_n = 0;
@@ -624,25 +652,19 @@ hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
   } else {
     a.tiles_n = (a.N + BN - 1) / BN;
   }
-  const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
-  switch (out_kind) {
-    case 0:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE, false>), grid, block, 0, stream, a);
-      break;
-    case 1:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false>), grid, block, 0, stream, a);
-      break;
-    case 3:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 3, ENGINE, false>), grid, block, 0, stream, a);
-      break;
-    case 4:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 4, ENGINE, false>), grid, block, 0, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false>), grid, block, 0, stream, a);
-      break;
-  }
-  return hipGetLastError();
+}
+
+// Deep prefetch (three or four stages in LDS) pays for the FP8 engine, whose
+// loop is short enough to wait on the copies; the F16 engine is bound by its
+// own issue (decode + MFMA) and keeps two stages.  A 128x128 tile with four
+// stages fills the CU's LDS, so it is used only when there is at most one
+// tile per CU -- otherwise two-stage tiles run two to a CU.
+template <int BM, int BN, int WM, int WN, int ENGINE>
+hipError_t launch_cfg(GemmArgs a, int out_kind, int num_cus, hipStream_t stream) {
+  set_tiles<BM, BN>(a);
+  const bool deep = ENGINE == 1 && (BM + BN > 256 || (int64_t)a.tiles_m * a.tiles_n <= num_cus);
+  if (deep) return launch_tiled<BM, BN, WM, WN, ENGINE, true>(a, out_kind, stream);
+  return launch_tiled<BM, BN, WM, WN, ENGINE, false>(a, out_kind, stream);
 }
 
 template <int BM, int WM, int WN, int ENGINE>
@@ -680,9 +702,9 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
     cfg = tiles(256, 256) >= want ? 1 : (tiles(256, 128) >= want ? 5 : 3);
   }
   switch (cfg) {
-    case 1: return launch_tiled<256, 256, 2, 4, ENGINE>(a, out_kind, stream);
-    case 5: return launch_tiled<256, 128, 4, 2, ENGINE>(a, out_kind, stream);
-    default: return launch_tiled<128, 128, 2, 2, ENGINE>(a, out_kind, stream);
+    case 1: return launch_cfg<256, 256, 2, 4, ENGINE>(a, out_kind, num_cus, stream);
+    case 5: return launch_cfg<256, 128, 4, 2, ENGINE>(a, out_kind, num_cus, stream);
+    default: return launch_cfg<128, 128, 2, 2, ENGINE>(a, out_kind, num_cus, stream);
   }
 }
 
