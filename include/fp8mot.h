@@ -149,7 +149,12 @@ int fp8_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
  * contiguous); y: [M, N] row-major, contiguous (leading dimension N).
  * K must be a multiple of 16.  d_sy is used only for FP8MOT_OUT_FP8 (NULL
  * there is FP8MOT_ERR_UNSUPPORTED) and ignored otherwise.  K == 0 writes
- * zeros.  `accum` selects the engine (fp8mot_acc). */
+ * zeros.  `accum` selects the engine (fp8mot_acc).  Order of the FP32 sum:
+ * along K, except for a GEMM with K > N and too few 128x128 output tiles to
+ * give each CU more than one, where the 128-K blocks at even and at odd
+ * positions are summed separately and the two sums added at the end (both
+ * orders are FP32 accumulation of the same exact products).  The order
+ * depends on (M, N, K) only, so equal shapes give equal bits. */
 int fp8_linear(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
                int64_t N, int64_t K, const float* d_sx, const float* d_sw,
                int out_kind, const float* d_sy, int accum, hipStream_t stream);
@@ -290,8 +295,9 @@ size_t qkv_fp8_workspace(int64_t M, int64_t H);
  *   qX = quant(x; sx); yq = linear(qX, wq; sx, sq); yk = ...; yv = ...
  * x: [M, H]; wq: [Nq, H]; wk: [Nk, H]; wv: [Nv, H]; yq: [M, Nq], yk: [M, Nk],
  * yv: [M, Nv], three separate contiguous BF16 tensors.  H multiple of 16.
- * The three GEMMs run as one grouped launch (bitwise what three fp8_linear
- * calls give).  A member with N == 0 is skipped and its pointers may be NULL.
+ * The three GEMMs run as one grouped launch, or as three launches when
+ * fp8_linear would split K for one of them; either way bitwise what three
+ * fp8_linear calls give.  A member with N == 0 is skipped and its pointers may be NULL.
  * Cross-attention, where k/v read a different tensor than q, must not use
  * this call: quantize each input separately and use fp8_linear.  `accum`
  * selects the GEMM engine (fp8mot_acc). */

@@ -342,8 +342,15 @@ int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
     nb[groups] = n3[p];
     ++groups;
   }
-  if (e == hipSuccess && groups > 0)
+  // A member that fp8_linear would run with K split over two wave groups is
+  // launched on its own, so that every output equals fp8_linear's bit for bit.
+  bool split = false;
+  for (int p = 0; p < groups; ++p) split = split || gemm_splits_k(M, nb[p], H, cus);
+  if (e == hipSuccess && groups > 0 && !split)
     e = launch_gemm_grouped(qx, groups, wb, yb, nb, M, H, d_sx, sb, accum, cus, stream);
+  for (int p = 0; p < groups && split && e == hipSuccess; ++p)
+    e = launch_gemm(qx, wb[p], yb[p], M, nb[p], H, d_sx, sb[p], FP8MOT_OUT_BF16, nullptr,
+                    accum, cus, stream);
   return hip_status(e);
 }
 

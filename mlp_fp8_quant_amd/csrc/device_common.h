@@ -52,22 +52,22 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
 }
 
 // Four FP32 values -> four E4M3 codes packed little-endian in a dword, using
-// the gfx950 conversion instruction.  Clamping to [-448, 448] first makes it
-// saturate; over every non-NaN FP32 input this gives exactly the codes of
-// e4m3_encode (checked by running both over all 2^32 bit patterns).  NaN
-// inputs are patched to 0x7F afterwards.
+// the gfx950 conversion instruction.  A NaN-propagating clamp to [-448, 448]
+// (IEEE-754 maximum / minimum) makes the conversion saturate and leaves NaN a
+// NaN, which the conversion turns into 0xFF; no finite input gives 0xFF
+// (-448 is 0xFE), so clearing the sign bit of every 0xFF byte yields 0x7F.
+// A byte is 0xFF exactly when its low seven bits plus one carry into bit 7
+// and its own bit 7 is set; the low-seven-bit sums cannot carry across
+// bytes.  Over every FP32 bit pattern, NaN included, this gives the codes of
+// e4m3_encode (checked on the hardware by running both over all 2^32).
+__device__ __forceinline__ float clamp448(float v) {
+  return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.0f), 448.0f);
+}
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
-  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  const float cc = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-  const float cd = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
-  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
-  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, (int)w, true);
-  if (a != a) w = (w & 0xFFFFFF00u) | 0x0000007Fu;
-  if (b != b) w = (w & 0xFFFF00FFu) | 0x00007F00u;
-  if (c != c) w = (w & 0xFF00FFFFu) | 0x007F0000u;
-  if (d != d) w = (w & 0x00FFFFFFu) | 0x7F000000u;
-  return w;
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), (int)w, true);
+  const uint32_t nan_bytes = (((w & 0x7F7F7F7Fu) + 0x01010101u) & w) & 0x80808080u;
+  return w ^ nan_bytes;
 }
 
 // SiLU(g) * u in FP32: g * (1 / (1 + exp(-g))) * u, with the hardware

@@ -68,6 +68,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kNumXcd = 8;      // MI355X: 8 XCDs
 constexpr int kGroupM = 8;      // tile rows per band
@@ -238,11 +239,17 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // scale per row of A and per row of B (per-token / per-channel).  FUSED: gate and up GEMMs of a gated MLP in one
 // tile (BN = 256 = 128 gate rows + 128 up rows of the same output columns)
 // whose epilogue applies SwiGLU and writes FP8, bit for bit what the separate
-// BF16 GEMMs followed by silu_mul_2in_fp8 produce.
-template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED, bool DEEP = false>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
+// BF16 GEMMs followed by silu_mul_2in_fp8 produce.  KSPL = 2: two groups of
+// WM x WN waves share the tile, group 0 taking the even 128-K stages and
+// group 1 the odd ones, each with its own stages in LDS; at the end group 1
+// hands its sums to group 0 through LDS, which adds them (even + odd) and
+// runs the epilogue.  That doubles the waves per CU (and the bytes in flight)
+// when there are too few tiles to give every CU more than one.
+template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED, bool DEEP = false,
+          int KSPL = 1>
+__global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g) {
   const int M = g.M, K = g.K;
-  constexpr int NW = WM * WN;
+  constexpr int NW = WM * WN;                   // waves per K group
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
   constexpr int STAGE = (BM + BN) * KS;
@@ -253,13 +260,20 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   constexpr int LPW = INS / NW;                            // ... per wave
   static_assert(LPW * NW == INS, "tile rows / waves");
   static_assert(!FUSED || (BN == 256 && FN % 2 == 0), "fused tiles pair gate/up blocks");
-  static_assert(NB * STAGE <= 160 * 1024, "stages fit the 160 KB LDS of a CU");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NB * STAGE];
-  auto stage_buf = [&](int b) -> uint8_t* { return smem + b * STAGE; };
+  static_assert(KSPL == 1 || (KSPL == 2 && !FUSED && !DEEP), "K split: plain tiles, two stages");
+  static_assert(KSPL * NB * STAGE <= 160 * 1024, "stages fit the 160 KB LDS of a CU");
+  static_assert(KSPL == 1 || NW * FM * FN * 16 * 64 * 4 <= KSPL * NB * STAGE,
+                "the K groups' sums fit the stage buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[KSPL * NB * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = KSPL == 1 ? 0 : wave_id / NW;    // K group
+  const int wave = wave_id - kg * NW;             // wave within its K group
   const int wm = wave / WN, wn = wave % WN;
+  auto stage_buf = [&](int b) -> uint8_t* { return smem + (kg * NB + b) * STAGE; };
+  // K group kg's local stage t is the tile's stage t * KSPL + kg
+  auto gstage = [&](int t) { return t * KSPL + kg; };
   int tm, tn;
   tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   // this tile's projection (a grouped launch walks the groups' tile columns)
@@ -443,14 +457,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   //    just freed, then read the first fragments of stage s + 1.
   // The MFMAs of a step are issued after these reads, so the barrier wait
   // overlaps the matrix pipe still working through the previous step.
-  const int KT = (K + KS - 1) / KS;
+  // local stages per K group (group 1 of an odd count runs one past the end
+  // of K, on zeros, so that both groups meet the same barriers)
+  const int KT = ((K + KS - 1) / KS + KSPL - 1) / KSPL;
   // have the epilogue's kernel arguments in registers before the loop, so no
   // scalar load is still pending inside it (that would turn every LDS wait
   // there into a wait for all LDS reads)
   asm volatile("" ::"s"(g.sx), "s"(gsw), "s"(g.sw2), "s"(g.sy), "s"(gCp));
 #pragma unroll
   for (int u = 0; u < NB; ++u)
-    if (u < KT) issue_stage(u, u);
+    if (u < KT) issue_stage(u, gstage(u));
   if (KT > 0) {
     wait_copies(LPW * (min(NB, KT) - 1));
     __syncthreads();
@@ -478,7 +494,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
             // the end of K they touch no memory and write zeros, into a
             // buffer nobody reads again -- at the last stage, where no
             // barrier has freed this buffer, into the next one instead.
-            mf(slot, std::true_type{}, s + 1 < KT ? u : (u + 1) % NB, s + NB);
+            mf(slot, std::true_type{}, s + 1 < KT ? u : (u + 1) % NB, gstage(s + NB));
           }
         }
       }
@@ -486,6 +502,36 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   }
   // no copy into LDS may still be on its way when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+  if constexpr (KSPL == 2) {
+    // Group 1's sums go through LDS to the wave of group 0 that holds the same
+    // blocks: 16-byte pieces, lane-major (conflict-free), over the stage
+    // buffers, which nobody reads or fills any more after this barrier.
+    __syncthreads();
+    v4f* red = reinterpret_cast<v4f*>(smem) + wave * (FM * FN * 4 * 64) + lane;
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            red[((i * FN + j) * 4 + q) * 64] =
+                (v4f){acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
+    __syncthreads();
+    if (kg == 1) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4f o = red[((i * FN + j) * 4 + q) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = __fadd_rn(acc[i][j][4 * q + e], o[e]);
+        }
+  }
 
   // ---- epilogue: y = fp32(acc * alpha), then the output format ----
   // Accumulator register v of 32x32 block (i, j) holds row
@@ -615,24 +661,24 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int ENGINE, bool DEEP>
+template <int BM, int BN, int WM, int WN, int ENGINE, bool DEEP, int KSPL>
 hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
-  const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
+  const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64 * KSPL);
   switch (out_kind) {
     case 0:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
       break;
     case 1:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
       break;
     case 3:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 3, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 3, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
       break;
     case 4:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 4, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 4, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false, DEEP>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
       break;
   }
   return hipGetLastError();
@@ -654,19 +700,6 @@ void set_tiles(GemmArgs& a) {
   }
 }
 
-// Deep prefetch (three or four stages in LDS) pays for the FP8 engine, whose
-// loop is short enough to wait on the copies; the F16 engine is bound by its
-// own issue (decode + MFMA) and keeps two stages.  A 128x128 tile with four
-// stages fills the CU's LDS, so it is used only when there is at most one
-// tile per CU -- otherwise two-stage tiles run two to a CU.
-template <int BM, int BN, int WM, int WN, int ENGINE>
-hipError_t launch_cfg(GemmArgs a, int out_kind, int num_cus, hipStream_t stream) {
-  set_tiles<BM, BN>(a);
-  const bool deep = ENGINE == 1 && (BM + BN > 256 || (int64_t)a.tiles_m * a.tiles_n <= num_cus);
-  if (deep) return launch_tiled<BM, BN, WM, WN, ENGINE, true>(a, out_kind, stream);
-  return launch_tiled<BM, BN, WM, WN, ENGINE, false>(a, out_kind, stream);
-}
-
 template <int BM, int WM, int WN, int ENGINE>
 hipError_t launch_fused(GemmArgs a, hipStream_t stream) {
   a.tiles_m = (a.M + BM - 1) / BM;
@@ -676,11 +709,45 @@ hipError_t launch_fused(GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+int64_t tiles_of(int64_t M, int64_t N, int bm, int bn) {
+  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
+
+int forced_env(const char* name) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : -1;
+}
+
 // Tile configuration per shape (MI355X, 256 CUs): the largest tile that
 // still gives about one workgroup per CU.  Measured on the workload shapes:
 // 256x256 tiles with 8 waves (two per SIMD) are fastest once there are
 // ~0.7 tiles per CU; below that 256x128 (8 waves) and then 128x128 (4 waves)
 // keep the CUs busy.  FP8MOT_GEMM_CFG=<1|5|3> forces one configuration (tuning).
+int pick_cfg(int64_t tiles_256x256, int64_t tiles_256x128, int num_cus) {
+  static const int forced = forced_env("FP8MOT_GEMM_CFG");
+  if (forced >= 0) return forced == 1 || forced == 5 ? forced : 3;
+  const int64_t want = (int64_t)num_cus * 7 / 10;
+  return tiles_256x256 >= want ? 1 : (tiles_256x128 >= want ? 5 : 3);
+}
+
+// Deep prefetch (three or four stages in LDS) pays for the FP8 engine, whose
+// loop is short enough to wait on the copies; the F16 engine is bound by its
+// own issue (decode + MFMA) and keeps two stages.  A 128x128 tile with four
+// stages fills the CU's LDS, so it is used only when there is at most one
+// tile per CU -- otherwise two-stage tiles run two to a CU.  A 128x128 tile
+// that has a CU to itself splits K over two wave groups instead (see
+// gemm_splits_k).
+template <int BM, int BN, int WM, int WN, int ENGINE>
+hipError_t launch_cfg(GemmArgs a, int out_kind, int num_cus, hipStream_t stream, bool split) {
+  set_tiles<BM, BN>(a);
+  if constexpr (BM + BN == 256) {
+    if (split) return launch_tiled<BM, BN, WM, WN, ENGINE, false, 2>(a, out_kind, stream);
+  }
+  const bool deep = ENGINE == 1 && (BM + BN > 256 || (int64_t)a.tiles_m * a.tiles_n <= num_cus);
+  if (deep) return launch_tiled<BM, BN, WM, WN, ENGINE, true, 1>(a, out_kind, stream);
+  return launch_tiled<BM, BN, WM, WN, ENGINE, false, 1>(a, out_kind, stream);
+}
+
 template <int ENGINE>
 hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stream) {
   auto tiles = [&](int bm, int bn) {
@@ -692,23 +759,24 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
     }
     return (int64_t)((a.M + bm - 1) / bm) * tn;
   };
-  static const int forced = [] {
-    const char* e = getenv("FP8MOT_GEMM_CFG");
-    return e ? atoi(e) : -1;
-  }();
-  int cfg = forced;
-  if (cfg < 0) {
-    const int64_t want = (int64_t)num_cus * 7 / 10;
-    cfg = tiles(256, 256) >= want ? 1 : (tiles(256, 128) >= want ? 5 : 3);
-  }
+  const int cfg = pick_cfg(tiles(256, 256), tiles(256, 128), num_cus);
+  const bool split = a.groups == 1 && gemm_splits_k(a.M, a.N, a.K, num_cus);
   switch (cfg) {
-    case 1: return launch_cfg<256, 256, 2, 4, ENGINE>(a, out_kind, num_cus, stream);
-    case 5: return launch_cfg<256, 128, 4, 2, ENGINE>(a, out_kind, num_cus, stream);
-    default: return launch_cfg<128, 128, 2, 2, ENGINE>(a, out_kind, num_cus, stream);
+    case 1: return launch_cfg<256, 256, 2, 4, ENGINE>(a, out_kind, num_cus, stream, false);
+    case 5: return launch_cfg<256, 128, 4, 2, ENGINE>(a, out_kind, num_cus, stream, false);
+    default: return launch_cfg<128, 128, 2, 2, ENGINE>(a, out_kind, num_cus, stream, split);
   }
 }
 
 }  // namespace
+
+bool gemm_splits_k(int64_t M, int64_t N, int64_t K, int num_cus) {
+  static const int forced = forced_env("FP8MOT_GEMM_SPLIT");   // 0: never, 1: any K (tuning)
+  if (forced == 0 || K <= KS) return false;
+  if (pick_cfg(tiles_of(M, N, 256, 256), tiles_of(M, N, 256, 128), num_cus) != 3) return false;
+  if (tiles_of(M, N, 128, 128) > num_cus) return false;
+  return K > N || forced == 1;
+}
 
 hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        int64_t M, int64_t N, int64_t K, const float* sx,
