@@ -98,13 +98,14 @@ typedef enum {
 
 /* Observer state, 16 bytes in device memory.  An all-zero state is a fresh
  * observer (the caller zero-fills it once).  `m` is the observed value,
- * `count` the number of calls folded in; `pending` is the library's own
- * reduction slot and is back at zero after each call; `reserved` stays 0. */
+ * `count` the number of calls folded in; `pending` (the call's amax) and
+ * `arrivals` (workgroups done) are the library's own reduction slots and are
+ * back at zero after each call. */
 typedef struct {
   float m;
   int32_t count;
   uint32_t pending;
-  uint32_t reserved;
+  uint32_t arrivals;
 } fp8mot_observer_state;
 
 /* ------------------------------------------------------------------ */
@@ -261,9 +262,12 @@ size_t gated_mlp_fp8_workspace(int64_t M, int64_t H, int64_t I);
  * projections the FP8 tensor; SiLU(G)*U emits FP8 at the down input scale).
  *   qX = quant(x; sx); G = linear(qX, wg; sx, sg); U = linear(qX, wu; sx, su)
  *   qH = silu_mul_2in(G, U; sh); y = linear(qH, wd; sh, sd)  (BF16 out)
- * Bitwise equal to those five calls (the gate and up GEMMs and the SwiGLU run
- * as one kernel whose epilogue rounds G and U to BF16 and applies the SwiGLU
- * exactly as the separate calls do; G and U are never written).
+ * Bitwise equal to those five calls when I >= H (the gate and up GEMMs and
+ * the SwiGLU run as one kernel whose epilogue rounds G and U to BF16 and
+ * applies the SwiGLU exactly as the separate calls do; G and U are never
+ * written).  With H > I and few tiles the separate gate/up fp8_linear calls
+ * sum K in two halves (see fp8_linear) while this kernel sums along K, so
+ * an SwiGLU code can then differ by one step.
  * x: [M, H]; wg, wu: [I, H]; wd: [H, I];
  * y: [M, H].  H and I multiples of 16.  ws: device workspace of at least
  * gated_mlp_fp8_workspace(M, H, I) bytes, 256-byte aligned.  `accum`
@@ -278,8 +282,8 @@ int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
  * ([PR] "What changed": one quantized activation handed to both
  * projections; the two-input SwiGLU emits FP8 for the down projection):
  *   qh = silu_mul_2in_fp8(linear(qx, wg; sx, sg), linear(qx, wu; sx, su); sh)
- * bitwise, computed by one kernel that shares each qx tile between the two
- * GEMMs and never writes G or U.  qx: E4M3 [M, H]; wg, wu: E4M3 [I, H];
+ * (bitwise when I >= H, as for gated_mlp_fp8), computed by one kernel that
+ * shares each qx tile between the two GEMMs and never writes G or U.  qx: E4M3 [M, H]; wg, wu: E4M3 [I, H];
  * qh: E4M3 [M, I].  H and I multiples of 16.  `accum` per fp8mot_acc. */
 int fp8_gate_up_swiglu(const uint8_t* qx, const uint8_t* wg, const float* d_sx,
                        const float* d_sg, const uint8_t* wu, const float* d_su,

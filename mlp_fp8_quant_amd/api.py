@@ -244,7 +244,8 @@ def silu_mul_fp8(x, s_out, out=None, alpha=None, beta=None):
 def fp8_gate_up_swiglu(qx, wg, sx, sg, wu, su, sh, out=None, accum=ACC_EXACT):
     """qh = SwiGLU-FP8 of the gate and up projections of an E4M3 activation
     qx [..., H] (wg, wu [I, H]); bitwise what fp8_linear (BF16 out) twice and
-    silu_mul_2in_fp8 give, in one kernel."""
+    silu_mul_2in_fp8 give when I >= H (with H > I and few tiles fp8_linear
+    sums K in two halves and a code can differ by one step), in one kernel."""
     _need(qx, "qx", torch.uint8)
     dev = qx.device
     _need(wg, "wg", torch.uint8, dev)

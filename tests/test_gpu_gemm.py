@@ -70,8 +70,12 @@ def test_identity_weight_returns_decoded_input(accum):
                           e4m3_decode(qx))
 
 
+# K > N with few tiles (129x127x144, 300x200x4096, 257x385x1040 with an odd
+# number of 128-K blocks, 64x48x1168, 512x256x8192) takes the kernel that
+# sums even and odd K blocks in two wave groups; the rest sums along K.
 SHAPES = [(1, 1, 16), (3, 5, 32), (17, 13, 48), (64, 64, 64), (128, 128, 128),
-          (129, 127, 144), (300, 200, 4096), (257, 385, 1040), (16, 17, 0)]
+          (129, 127, 144), (300, 200, 4096), (257, 385, 1040), (16, 17, 0),
+          (64, 48, 1168), (512, 256, 8192)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

@@ -258,7 +258,15 @@ def test_gate_up_swiglu_ragged_equals_parts(accum, M, I, H):
     qh = fp8.fp8_gate_up_swiglu(qx, dg, dsx, dsg, du, dsu, dsh, accum=accum)
     G = fp8.fp8_linear(qx, dg, dsx, dsg, accum=accum)
     U = fp8.fp8_linear(qx, du, dsx, dsu, accum=accum)
-    assert torch.equal(qh, fp8.silu_mul_2in_fp8(G, U, dsh))
+    parts = fp8.silu_mul_2in_fp8(G, U, dsh)
+    if I >= H:
+        # the separate gate and up GEMMs sum along K as the fused kernel does
+        assert torch.equal(qh, parts)
+    else:
+        # H > I with few tiles: fp8_linear sums the even and odd K blocks
+        # separately, so G and U may differ in the last FP32 bit and a code
+        # may move by a step
+        check_fp8_tolerance(host_u8(qh), host_u8(parts))
 
 
 @pytest.mark.parametrize("ns", [(384, 128, 96), (4096, 1024, 1024), (200, 0, 72)])
