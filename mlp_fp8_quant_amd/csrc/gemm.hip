@@ -632,8 +632,39 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
           }
         }
       }
+  } else if constexpr (OUT == 1) {
+    // FP8: the four rows of a column are encoded into one dword, transposed
+    // in the quad so that each lane stores four consecutive columns of one
+    // row (4 bytes).  Rows whose width is not a multiple of 4 take byte
+    // stores.
+    const float sy = *g.sy;
+    const bool vec_ok = (N % 4) == 0 && (ldc % 4) == 0;
+    const int col_q = n0 + wn * WTN + ((lane & 31) & ~3);   // + j*32
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          float h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = __fmul_rn(acc[i][j][4 * q + e], alpha) / sy;   // IEEE division
+          const uint32_t w = quad_transpose_bytes(e4m3_pack4(h[0], h[1], h[2], h[3]), qt);
+          const int row = row_l + i * 32 + q * 8 + qt;
+          const int col = col_q + j * 32;
+          if (vec_ok) {
+            const int off = (m0 + row < M && col < N) ? row * ldc + col : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(w, rc_rs, off, 0, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int off = (m0 + row < M && col + e < N) ? row * ldc + col + e : kOOB;
+              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w >> (8 * e)), rc_rs, off, 0, 0);
+            }
+          }
+        }
   } else {
-    const float sy = (OUT == 1) ? *g.sy : 1.0f;
+    // FP32 (per-tensor or per-row scales): one dword per element
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -651,10 +682,7 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
             const int off = ok ? (row * ldc + n0 + col) * ESZ : kOOB;
             const float al = ROWWISE ? __fmul_rn(__int_as_float(sxr[e]), swc[j]) : alpha;
             const float y = __fmul_rn(acc[i][j][v], al);
-            if constexpr (OUT == 1)
-              __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e4m3_encode(y / sy), rc_rs, off, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rc_rs, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), rc_rs, off, 0, 0);
           }
         }
       }

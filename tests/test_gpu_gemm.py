@@ -135,6 +135,23 @@ def test_fp8_output_epilogue(accum):
     assert np.all((o(got) >= o(lo) - 1) & (o(got) <= o(hi) + 1))
 
 
+@pytest.mark.parametrize("accum", ENGINES)
+@pytest.mark.parametrize("M,N,K", [(257, 385, 1040), (129, 127, 144), (64, 48, 1168),
+                                   (300, 200, 4096), (512, 1024, 512)])
+def test_fp8_output_is_the_encoded_f32_output(accum, M, N, K):
+    # the FP8 epilogue encodes fp32(acc * alpha) / s_y: bit for bit the
+    # encoding (oracle encoder, IEEE FP32 division) of the same kernel's FP32
+    # output, on ragged widths (byte stores) and vector ones alike
+    dev = device()
+    rng = np.random.default_rng(M + 7 * N + K)
+    qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx, sw, sy = np.float32(0.0213), np.float32(1.7e-4), np.float32(0.37)
+    out = _run(qa, qb, sx, sw, dev, kinds=(fp8.OUT_F32, fp8.OUT_FP8), sy=sy, accum=accum)
+    y32 = host_f32(out[fp8.OUT_F32])
+    want = e4m3_encode((y32 / sy).astype(np.float32))
+    assert np.array_equal(host_u8(out[fp8.OUT_FP8]), want)
+
+
 def _linear_case(x_bits, w_bits, dev, rows=None, accum=fp8.ACC_EXACT):
     """Quantize x and w as the method does and compare one projection."""
     sx = olin.scale_from_amax(olin.amax_f32(x_bits))

@@ -35,6 +35,29 @@ def test_quant_exhaustive_random_scales():
         assert np.array_equal(host_u8(q), olin.quant_static(ALL_BF16, s)), s
 
 
+@pytest.mark.parametrize("m", [1.0, 3.0, 0.0123])
+def test_quant_exhaustive_scales_next_to_exact(m):
+    # s = m * (1 + k 2^-23): x / s lands within a few FP32 units of the E4M3
+    # rounding boundaries that BF16 inputs sit on exactly (every midpoint
+    # has 5 significant bits), where a quotient taken through 1/s can round
+    # the other way; the codes must still be those of the IEEE quotient
+    dev = device()
+    x = to_dev_bf16(ALL_BF16, dev)
+    for k in range(-6, 7):
+        s = np.float32(m) * np.float32(1.0 + k * 2.0 ** -23)
+        q = fp8.fp8_quant_static(x, scalar(s, dev))
+        assert np.array_equal(host_u8(q), olin.quant_static(ALL_BF16, s)), (m, k)
+
+
+@pytest.mark.parametrize("scale", [1e-39, 3e38, 2.0 ** -126, 2.0 ** 126])
+def test_quant_exhaustive_extreme_scales(scale):
+    # 1/s subnormal or infinite: every element takes the IEEE division
+    dev = device()
+    s = np.float32(scale)
+    q = fp8.fp8_quant_static(to_dev_bf16(ALL_BF16, dev), scalar(s, dev))
+    assert np.array_equal(host_u8(q), olin.quant_static(ALL_BF16, s))
+
+
 @pytest.mark.parametrize("n", [0, 1, 7, 15, 16, 17, 255, 4097, 1_000_003])
 def test_quant_ragged_lengths(n):
     dev = device()
