@@ -98,14 +98,13 @@ typedef enum {
 
 /* Observer state, 16 bytes in device memory.  An all-zero state is a fresh
  * observer (the caller zero-fills it once).  `m` is the observed value,
- * `count` the number of calls folded in; `pending` (the call's amax) and
- * `arrivals` (workgroups done) are the library's own reduction slots and are
- * back at zero after each call. */
+ * `count` the number of calls folded in; `pending` is the library's own
+ * reduction slot and is back at zero after each call; `reserved` stays 0. */
 typedef struct {
   float m;
   int32_t count;
   uint32_t pending;
-  uint32_t arrivals;
+  uint32_t reserved;
 } fp8mot_observer_state;
 
 /* ------------------------------------------------------------------ */

@@ -293,36 +293,11 @@ __global__ __launch_bounds__(kThreads) void requant_onto_max_kernel(
   }
 }
 
-// Folds the call's amax into the state and clears the call's slots.
-__device__ __forceinline__ void observer_fold(fp8mot_observer_state_dev* st, int mode, float c) {
-  const float a = __uint_as_float(__hip_atomic_load(&st->pending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  float m = st->m;
-  if (st->count == 0) {
-    m = a;
-  } else if (mode == 0) {
-    m = (a != a || m != m) ? __builtin_nanf("") : (a > m ? a : m);
-  } else {
-    const float d = __fsub_rn(a, m);
-    const float p = __fmul_rn(c, d);
-    m = __fadd_rn(m, p);
-  }
-  st->m = m;
-  st->count = st->count + 1;
-  __hip_atomic_store(&st->pending, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&st->arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Block-wide max of non-negative FP32 bit patterns (integer order == value
 // order for non-negative floats; NaN patterns sort above +Inf) into the
 // state's pending slot.  Only a block that can raise the running value
-// issues the atomic, so the atomics do not serialize on one address.  Then
-// the block counts itself in; the last block to arrive (every other block's
-// atomic max is ordered before its count by the release fence, and before
-// the last block's reads by the acquire fence) folds the amax into the state
-// -- no wait on other blocks, so nothing can hang on a block not yet
-// resident.
-__device__ __forceinline__ void block_max_fold(uint32_t v, fp8mot_observer_state_dev* st,
-                                               int mode, float c) {
+// issues the atomic, so the atomics do not serialize on one address.
+__device__ __forceinline__ void block_max_to(uint32_t v, uint32_t* dst) {
   __shared__ uint32_t red[kThreads / 64];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -336,23 +311,15 @@ __device__ __forceinline__ void block_max_fold(uint32_t v, fp8mot_observer_state
     uint32_t m = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) m = m > red[w] ? m : red[w];
-    if (m > __hip_atomic_load(&st->pending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-      atomicMax(&st->pending, m);
-    __atomic_thread_fence(__ATOMIC_RELEASE);
-    const uint32_t done = __hip_atomic_fetch_add(&st->arrivals, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    if (done == gridDim.x - 1) {
-      __atomic_thread_fence(__ATOMIC_ACQUIRE);
-      observer_fold(st, mode, c);
-    }
+    if (m > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(dst, m);
   }
 }
 
 // amax over BF16: max of (bits & 0x7FFF) as integers is max |x| exactly.
 // Four 128-bit loads per thread per step.
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(
-    const uint16_t* __restrict__ x, int64_t n, fp8mot_observer_state_dev* st, int mode,
-    float c) {
+    const uint16_t* __restrict__ x, int64_t n, uint32_t* __restrict__ pending) {
   const int64_t units = n >> 3;                 // 8-element units
   const int64_t stride = (int64_t)gridDim.x * kThreads * 4;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
@@ -383,14 +350,14 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(
       m = m > v ? m : v;
     }
   }
-  block_max_fold(m << 16, st, mode, c);
+  block_max_to(m << 16, pending);
 }
 
 // amax of silu(g) * u in FP32 (as silu_mul_kernel evaluates it).  Four
 // 8-element units per thread per step.
 __global__ __launch_bounds__(kThreads) void amax_swiglu_kernel(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ u, int64_t n,
-    fp8mot_observer_state_dev* st, int mode, float c) {
+    uint32_t* __restrict__ pending) {
   const int64_t units = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * kThreads * 4;
   const u32x4* gv = reinterpret_cast<const u32x4*>(g);
@@ -429,7 +396,26 @@ __global__ __launch_bounds__(kThreads) void amax_swiglu_kernel(
       m = m > v ? m : v;
     }
   }
-  block_max_fold(m, st, mode, c);
+  block_max_to(m, pending);
+}
+
+// Folds the pending amax into the state and clears the slot.  One thread.
+__global__ void observer_update_kernel(fp8mot_observer_state_dev* st, int mode,
+                                       float c) {
+  const float a = __uint_as_float(st->pending);
+  float m = st->m;
+  if (st->count == 0) {
+    m = a;
+  } else if (mode == 0) {
+    m = (a != a || m != m) ? __builtin_nanf("") : (a > m ? a : m);
+  } else {
+    const float d = __fsub_rn(a, m);
+    const float p = __fmul_rn(c, d);
+    m = __fadd_rn(m, p);
+  }
+  st->m = m;
+  st->count = st->count + 1;
+  st->pending = 0u;
 }
 
 __global__ void scale_from_state_kernel(const fp8mot_observer_state_dev* st,
@@ -505,17 +491,25 @@ hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,
                           fp8mot_observer_state_dev* st, int mode, float c,
                           int max_blocks, hipStream_t stream) {
   // Every workgroup ends in (at most) one atomic on the same word, and those
-  // serialize at its L2 slice: keep the grid at two workgroups per CU (about
-  // as fast on the loads as more, measured on MI355X, with 8x fewer atomics).
-  const int amax_blocks = max_blocks / 4 > 0 ? max_blocks / 4 : 1;
-  // One launch: the last workgroup to finish folds the amax into the state.
+  // serialize: keep the grid at about one workgroup per 32K elements, and at
+  // most two per CU (measured on MI355X: for 4M elements 128 workgroups take
+  // 6.2 us and 512 take 8.6; for 52M, 512 take 17.8 us and 256 take 23.8).
+  // Folding the amax into the state in the last workgroup to finish, instead
+  // of the one-thread kernel below, was slower at both sizes: the arrival
+  // count is one more atomic per workgroup on one word.
+  const int64_t want = (n + 32767) / 32768;
+  const int cap = max_blocks / 4 > 0 ? max_blocks / 4 : 1;
+  const int amax_blocks = want < 1 ? 1 : (want < cap ? (int)want : cap);
   if (u == nullptr) {
     hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid_for(n >> 5, amax_blocks)),
-                       dim3(kThreads), 0, stream, x, n, st, mode, c);
+                       dim3(kThreads), 0, stream, x, n, &st->pending);
   } else {
     hipLaunchKernelGGL(amax_swiglu_kernel, dim3(grid_for(n >> 5, amax_blocks)),
-                       dim3(kThreads), 0, stream, x, u, n, st, mode, c);
+                       dim3(kThreads), 0, stream, x, u, n, &st->pending);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(observer_update_kernel, dim3(1), dim3(1), 0, stream, st, mode, c);
   return hipGetLastError();
 }
 
