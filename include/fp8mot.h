@@ -150,8 +150,9 @@ int fp8_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
  * K must be a multiple of 16.  d_sy is used only for FP8MOT_OUT_FP8 (NULL
  * there is FP8MOT_ERR_UNSUPPORTED) and ignored otherwise.  K == 0 writes
  * zeros.  `accum` selects the engine (fp8mot_acc).  Order of the FP32 sum:
- * along K, except for a GEMM with K > N and too few 128x128 output tiles to
- * give each CU more than one, where the 128-K blocks at even and at odd
+ * along K, except for a GEMM with K > N whose 128-row output tiles (128x128,
+ * or 128x64 when even those are too few) give no CU more than one, where the
+ * 128-K blocks at even and at odd
  * positions are summed separately and the two sums added at the end (both
  * orders are FP32 accumulation of the same exact products).  The order
  * depends on (M, N, K) only, so equal shapes give equal bits. */

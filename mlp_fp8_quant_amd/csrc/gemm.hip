@@ -749,26 +749,30 @@ int forced_env(const char* name) {
 // Tile configuration per shape (MI355X, 256 CUs): the largest tile that
 // still gives about one workgroup per CU.  Measured on the workload shapes:
 // 256x256 tiles with 8 waves (two per SIMD) are fastest once there are
-// ~0.7 tiles per CU; below that 256x128 (8 waves) and then 128x128 (4 waves)
-// keep the CUs busy.  FP8MOT_GEMM_CFG=<1|5|3> forces one configuration (tuning).
-int pick_cfg(int64_t tiles_256x256, int64_t tiles_256x128, int num_cus) {
+// ~0.7 tiles per CU; below that 256x128 (8 waves), then 128x128 and 128x64
+// (4 waves; 512x4096x4096: 33.9 -> 25.8 us, 512x4096x12288: 72.7 -> 55.6 us
+// with 128x64) keep the CUs busy.  FP8MOT_GEMM_CFG=<1|5|3|6> forces one
+// configuration (tuning; 6 is 128x64).
+int pick_cfg(int64_t tiles_256x256, int64_t tiles_256x128, int64_t tiles_128x128, int num_cus) {
   static const int forced = forced_env("FP8MOT_GEMM_CFG");
-  if (forced >= 0) return forced == 1 || forced == 5 ? forced : 3;
+  if (forced >= 0) return forced == 1 || forced == 5 || forced == 6 ? forced : 3;
   const int64_t want = (int64_t)num_cus * 7 / 10;
-  return tiles_256x256 >= want ? 1 : (tiles_256x128 >= want ? 5 : 3);
+  if (tiles_256x256 >= want) return 1;
+  if (tiles_256x128 >= want) return 5;
+  return tiles_128x128 >= want ? 3 : 6;
 }
 
 // Deep prefetch (three or four stages in LDS) pays for the FP8 engine, whose
 // loop is short enough to wait on the copies; the F16 engine is bound by its
 // own issue (decode + MFMA) and keeps two stages.  A 128x128 tile with four
 // stages fills the CU's LDS, so it is used only when there is at most one
-// tile per CU -- otherwise two-stage tiles run two to a CU.  A 128x128 tile
+// tile per CU -- otherwise two-stage tiles run two to a CU.  A 128-row tile
 // that has a CU to itself splits K over two wave groups instead (see
 // gemm_splits_k).
 template <int BM, int BN, int WM, int WN, int ENGINE>
 hipError_t launch_cfg(GemmArgs a, int out_kind, int num_cus, hipStream_t stream, bool split) {
   set_tiles<BM, BN>(a);
-  if constexpr (BM + BN == 256) {
+  if constexpr (BM == 128) {
     if (split) return launch_tiled<BM, BN, WM, WN, ENGINE, false, 2>(a, out_kind, stream);
   }
   const bool deep = ENGINE == 1 && (BM + BN > 256 || (int64_t)a.tiles_m * a.tiles_n <= num_cus);
@@ -787,11 +791,12 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
     }
     return (int64_t)((a.M + bm - 1) / bm) * tn;
   };
-  const int cfg = pick_cfg(tiles(256, 256), tiles(256, 128), num_cus);
+  const int cfg = pick_cfg(tiles(256, 256), tiles(256, 128), tiles(128, 128), num_cus);
   const bool split = a.groups == 1 && gemm_splits_k(a.M, a.N, a.K, num_cus);
   switch (cfg) {
     case 1: return launch_cfg<256, 256, 2, 4, ENGINE>(a, out_kind, num_cus, stream, false);
     case 5: return launch_cfg<256, 128, 4, 2, ENGINE>(a, out_kind, num_cus, stream, false);
+    case 6: return launch_cfg<128, 64, 2, 2, ENGINE>(a, out_kind, num_cus, stream, split);
     default: return launch_cfg<128, 128, 2, 2, ENGINE>(a, out_kind, num_cus, stream, split);
   }
 }
@@ -801,8 +806,10 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
 bool gemm_splits_k(int64_t M, int64_t N, int64_t K, int num_cus) {
   static const int forced = forced_env("FP8MOT_GEMM_SPLIT");   // 0: never, 1: any K (tuning)
   if (forced == 0 || K <= KS) return false;
-  if (pick_cfg(tiles_of(M, N, 256, 256), tiles_of(M, N, 256, 128), num_cus) != 3) return false;
-  if (tiles_of(M, N, 128, 128) > num_cus) return false;
+  const int cfg = pick_cfg(tiles_of(M, N, 256, 256), tiles_of(M, N, 256, 128),
+                           tiles_of(M, N, 128, 128), num_cus);
+  if (cfg != 3 && cfg != 6) return false;
+  if (tiles_of(M, N, 128, cfg == 3 ? 128 : 64) > num_cus) return false;
   return K > N || forced == 1;
 }
 

@@ -57,8 +57,9 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
 
 // True when launch_gemm of this shape splits K over two wave groups of one
 // workgroup: the sums of the even and of the odd 128-K stages are added at
-// the end instead of one running sum over K.  That happens for 128x128 tiles
-// with at most one tile per CU and K > N (a down projection short of tiles).
+// the end instead of one running sum over K.  That happens for 128x128 or
+// 128x64 tiles with at most one tile per CU and K > N (a down projection
+// short of tiles).
 // Callers that promise bitwise equality between two launch shapes check it.
 bool gemm_splits_k(int64_t M, int64_t N, int64_t K, int num_cus);
 
