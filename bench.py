@@ -200,6 +200,7 @@ def main():
     large = None if args.no_large else elementwise_large(fp8, torch, dev, stream)
     rowwise = None if args.no_large else per_row_fp8(fp8, torch, dev, stream, M, H, I)
     topology = None if args.no_large else fused_topology(fp8, torch, dev, stream, qx, sx, sh, q, s)
+    big_mlp = None if args.no_large else large_mlp(fp8, torch, dev, stream)
 
     if args.copy_calib_mb > 0:
         n = args.copy_calib_mb << 20
@@ -225,6 +226,7 @@ def main():
         "elementwise_large": large,
         "per_row_fp8": rowwise,
         "fused_topology": topology,
+        "large_mlp": big_mlp,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out))
@@ -334,6 +336,75 @@ def per_row_fp8(fp8, torch, dev, stream, M, H, I):
         us = timed(lambda r: fp8.fp8_linear_rowwise(qx, qw, sx, sw, out=y, accum=eng), 20)
         out[f"linear_rowwise_{name}_{M}x{I}x{H}"] = {"us": us, "TFLOP/s": fl / us / 1e6}
     del x, w, qx, qw, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def large_mlp(fp8, torch, dev, stream):
+    """The large compute-bound gated MLP (X [16384, 5120] N(0,1) with 0.5%
+    x20 outliers; gate/up [25600, 5120] and down [5120, 25600] N(0, 0.015),
+    RTN per tensor on the GPU; shared gate/up input scale amax(X)/448; down
+    input scale amax(silu(G) * U)/448 from the library's own observer on this
+    X): average time of the whole gated_mlp_fp8 call and of its two GEMM
+    launches, both engines.  Inputs are drawn on the GPU (seeded) for speed."""
+    M, H, I = 16384, 5120, 25600
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+
+    def timed(f, reps=4):
+        f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    xf = torch.randn((M, H), device=dev, generator=gen)
+    xf = torch.where(torch.rand((M, H), device=dev, generator=gen) < 0.005, xf * 20, xf)
+    x = xf.to(torch.bfloat16)
+    del xf
+    q, s = {}, {}
+    for k, shape in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        w = (torch.randn(shape, device=dev, generator=gen) * 0.015).to(torch.bfloat16)
+        q[k], s[k] = fp8.rtn_weight(w)
+        del w
+    st = fp8.new_observer_state(dev)
+    fp8.fp8_observe(x, st, fp8.OBS_MAX)
+    sx = fp8.fp8_scale_from_state(st)
+    qx = fp8.fp8_quant_static(x, sx)
+    G = fp8.fp8_linear(qx, q["gate"], sx, s["gate"])
+    U = fp8.fp8_linear(qx, q["up"], sx, s["up"])
+    sth = fp8.new_observer_state(dev)
+    fp8.fp8_observe_swiglu(G, U, sth, fp8.OBS_MAX)
+    sh = fp8.fp8_scale_from_state(sth)
+    del G, U
+    torch.cuda.empty_cache()
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(fp8.gated_mlp_fp8_workspace(M, H, I), dtype=torch.uint8, device=dev)
+    qh = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    gemm_flops = 3 * 2.0 * M * I * H
+    out = {"workload": f"large_mlp_M{M}_H{H}_I{I}", "gemm_flops": gemm_flops}
+    for name, acc, peak in (("exact", fp8.ACC_EXACT, F16_PEAK_TFLOPS),
+                            ("fp8_mfma", fp8.ACC_FP8_MFMA, FP8_PEAK_TFLOPS)):
+        t = timed(lambda: fp8.gated_mlp_fp8(x, sx, q["gate"], s["gate"], q["up"], s["up"], sh,
+                                            q["down"], s["down"], out=y, workspace=ws, accum=acc))
+        tf = timed(lambda: fp8.fp8_gate_up_swiglu(qx, q["gate"], sx, s["gate"], q["up"], s["up"],
+                                                  sh, out=qh, accum=acc))
+        td = timed(lambda: fp8.fp8_linear(qh, q["down"], sh, s["down"], out=y, accum=acc))
+        f_fused = 2 * 2.0 * M * I * H / (tf * 1e-6) / 1e12
+        f_down = 2.0 * M * I * H / (td * 1e-6) / 1e12
+        out[name] = {
+            "gated_mlp_us": t, "TFLOP/s": gemm_flops / (t * 1e-6) / 1e12,
+            "gate_up_swiglu_us": tf, "gate_up_swiglu_TFLOP/s": f_fused,
+            "gate_up_swiglu_frac_peak": f_fused / peak,
+            "down_us": td, "down_TFLOP/s": f_down, "down_frac_peak": f_down / peak,
+            "peak_TFLOP/s": peak,
+        }
+    del x, qx, qh, y, ws, q
     torch.cuda.empty_cache()
     return out
 
