@@ -345,7 +345,7 @@ int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
   // A member that fp8_linear would run with K split over two wave groups is
   // launched on its own, so that every output equals fp8_linear's bit for bit.
   bool split = false;
-  for (int p = 0; p < groups; ++p) split = split || gemm_splits_k(M, nb[p], H, cus);
+  for (int p = 0; p < groups; ++p) split = split || gemm_splits_k(M, nb[p], H, cus, accum);
   if (e == hipSuccess && groups > 0 && !split)
     e = launch_gemm_grouped(qx, groups, wb, yb, nb, M, H, d_sx, sb, accum, cus, stream);
   for (int p = 0; p < groups && split && e == hipSuccess; ++p)

@@ -792,7 +792,7 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
     return (int64_t)((a.M + bm - 1) / bm) * tn;
   };
   const int cfg = pick_cfg(tiles(256, 256), tiles(256, 128), tiles(128, 128), num_cus);
-  const bool split = a.groups == 1 && gemm_splits_k(a.M, a.N, a.K, num_cus);
+  const bool split = a.groups == 1 && gemm_splits_k(a.M, a.N, a.K, num_cus, ENGINE);
   switch (cfg) {
     case 1: return launch_cfg<256, 256, 2, 4, ENGINE>(a, out_kind, num_cus, stream, false);
     case 5: return launch_cfg<256, 128, 4, 2, ENGINE>(a, out_kind, num_cus, stream, false);
@@ -803,12 +803,16 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
 
 }  // namespace
 
-bool gemm_splits_k(int64_t M, int64_t N, int64_t K, int num_cus) {
+bool gemm_splits_k(int64_t M, int64_t N, int64_t K, int num_cus, int accum) {
   static const int forced = forced_env("FP8MOT_GEMM_SPLIT");   // 0: never, 1: any K (tuning)
   if (forced == 0 || K <= KS) return false;
   const int cfg = pick_cfg(tiles_of(M, N, 256, 256), tiles_of(M, N, 256, 128),
                            tiles_of(M, N, 128, 128), num_cus);
-  if (cfg != 3 && cfg != 6) return false;
+  // 128x64 tiles split K for the exact engine only: the FP8 engine's four
+  // 24 KB stages in LDS serve it better there (512x4096x12288: 48.1 us split,
+  // 41.1 us with four stages), while at 128x128 the split wins for both
+  // engines (2048x2048x8192 FP8 engine: 42.0 against 46.5 us).
+  if (cfg != 3 && !(cfg == 6 && accum != 1)) return false;   // 1: FP8 engine
   if (tiles_of(M, N, 128, cfg == 3 ? 128 : 64) > num_cus) return false;
   return K > N || forced == 1;
 }

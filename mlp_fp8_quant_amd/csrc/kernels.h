@@ -55,13 +55,13 @@ hipError_t launch_gemm(const uint8_t* qa, const uint8_t* qb, void* y,
                        const float* sw, int out_kind, const float* sy,
                        int accum, int num_cus, hipStream_t stream, int64_t ldc = 0);
 
-// True when launch_gemm of this shape splits K over two wave groups of one
-// workgroup: the sums of the even and of the odd 128-K stages are added at
-// the end instead of one running sum over K.  That happens for 128x128 or
-// 128x64 tiles with at most one tile per CU and K > N (a down projection
-// short of tiles).
+// True when launch_gemm of this shape and accumulation engine splits K over
+// two wave groups of one workgroup: the sums of the even and of the odd 128-K
+// stages are added at the end instead of one running sum over K.  That
+// happens for 128x128 tiles (either engine) or 128x64 tiles (exact engine)
+// with at most one tile per CU and K > N (a down projection short of tiles).
 // Callers that promise bitwise equality between two launch shapes check it.
-bool gemm_splits_k(int64_t M, int64_t N, int64_t K, int num_cus);
+bool gemm_splits_k(int64_t M, int64_t N, int64_t K, int num_cus, int accum);
 
 // Up to three BF16-output GEMMs of the same A in one launch (split Q/K/V):
 // y[p] [M, N[p]] = (qa . qb[p]^T) * (sx * sw[p]); groups with N[p] == 0 must
