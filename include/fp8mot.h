@@ -38,6 +38,12 @@
  *  - Sizes are int64_t element counts.  Negative sizes are
  *    FP8MOT_ERR_INVALID_ARG; an empty tensor (a zero size) is a valid no-op
  *    and then data pointers may be NULL.
+ *  - GEMM size limits (fp8_linear and every call built on it): M, N, K at
+ *    most INT32_MAX; 256 * K below 0x7FFFF000 (K <= 8,388,576); 256 output
+ *    rows below 0x7FFFF000 bytes (row length ldc = N, or the ldc argument,
+ *    times 1, 2 or 4 bytes for FP8, BF16, FP32 output); at most INT32_MAX
+ *    tiles of 128 x 64.  The kernels address one tile's rows with 32-bit
+ *    offsets; larger sizes are FP8MOT_ERR_INVALID_ARG, never wrapped.
  *  - Only gfx950 devices are supported; any other device gives
  *    FP8MOT_ERR_UNSUPPORTED.
  *  - The library is reentrant: calls on different streams may overlap.
@@ -56,7 +62,7 @@ extern "C" {
 
 typedef enum {
   FP8MOT_OK = 0,
-  FP8MOT_ERR_INVALID_ARG = 1,    /* NULL pointer, negative size, K % 16 != 0, bad enum, non-finite c */
+  FP8MOT_ERR_INVALID_ARG = 1,    /* NULL pointer, negative or too large size, K % 16 != 0, bad enum, non-finite c */
   FP8MOT_ERR_MISALIGNED = 2,     /* a tensor base pointer is not 16-byte aligned */
   FP8MOT_ERR_SCALE_MISMATCH = 3, /* a shared-quantization group's input scales differ */
   FP8MOT_ERR_UNSUPPORTED = 4,    /* NULL scale (dynamic quantization) or non-gfx950 device */

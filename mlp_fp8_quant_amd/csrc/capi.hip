@@ -71,6 +71,22 @@ MlpLayout mlp_layout(int64_t M, int64_t H, int64_t I) {
 }
 
 // Validation shared by the GEMM entry points.
+// The GEMM kernels address one tile's operand rows (at most 256 rows of K
+// codes) and its output rows (at most 256 rows of ldc elements of esz bytes)
+// with 32-bit byte offsets that must stay below their out-of-range sentinel
+// (0x7FFFFFF0), and number their tiles (128 x 64 at the smallest) with a
+// 32-bit workgroup index.  Larger sizes are refused rather than wrapped.
+constexpr int64_t kTileWindowBytes = 0x7FFFF000;
+bool gemm_sizes_ok(int64_t M, int64_t N, int64_t K, int64_t ldc, int esz) {
+  if (256 * K >= kTileWindowBytes) return false;
+  if (256 * ldc * esz >= kTileWindowBytes) return false;
+  return ((M + 127) / 128) * ((N + 63) / 64) <= INT32_MAX;
+}
+
+int out_bytes(int out_kind) {
+  return out_kind == FP8MOT_OUT_FP8 ? 1 : (out_kind == FP8MOT_OUT_BF16 ? 2 : 4);
+}
+
 int check_linear(const uint8_t* qx, const uint8_t* qw, const void* y, int64_t M,
                  int64_t N, int64_t K, const float* sx, const float* sw,
                  int out_kind, const float* sy, int accum) {
@@ -80,6 +96,7 @@ int check_linear(const uint8_t* qx, const uint8_t* qw, const void* y, int64_t M,
   if (out_kind == FP8MOT_OUT_FP8 && sy == nullptr) return FP8MOT_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || (K % 16) != 0) return FP8MOT_ERR_INVALID_ARG;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return FP8MOT_ERR_INVALID_ARG;
+  if (!gemm_sizes_ok(M, N, K, N, out_bytes(out_kind))) return FP8MOT_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FP8MOT_OK;
   if (y == nullptr || (K > 0 && (qx == nullptr || qw == nullptr)))
     return FP8MOT_ERR_INVALID_ARG;
@@ -99,7 +116,7 @@ int fp8mot_init(int device) {
 const char* fp8mot_status_string(int status) {
   switch (status) {
     case FP8MOT_OK: return "ok";
-    case FP8MOT_ERR_INVALID_ARG: return "invalid argument (NULL pointer, negative size, K % 16 != 0, bad enum or non-finite constant)";
+    case FP8MOT_ERR_INVALID_ARG: return "invalid argument (NULL pointer, negative or too large size, K % 16 != 0, bad enum or non-finite constant)";
     case FP8MOT_ERR_MISALIGNED: return "tensor base pointer not 16-byte aligned";
     case FP8MOT_ERR_SCALE_MISMATCH: return "input scales of a shared-quantization group differ";
     case FP8MOT_ERR_UNSUPPORTED: return "unsupported: NULL scale (dynamic quantization) or non-gfx950 device";
@@ -159,6 +176,7 @@ int fp8_linear_ldc(const uint8_t* qx, const uint8_t* qw, void* y, int64_t M,
   if (st != FP8MOT_OK) return st;
   if (ldc < N || ldc > INT32_MAX) return FP8MOT_ERR_INVALID_ARG;
   if (M > 0 && ldc > INT64_MAX / M) return FP8MOT_ERR_INVALID_ARG;
+  if (!gemm_sizes_ok(M, N, K, ldc, out_bytes(out_kind))) return FP8MOT_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FP8MOT_OK;
   int cus = 0;
   st = current_device(&cus);
@@ -245,6 +263,8 @@ int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
   if (M < 0 || H < 0 || I < 0 || (H % 16) != 0 || (I % 16) != 0)
     return FP8MOT_ERR_INVALID_ARG;
   if (M > INT32_MAX || H > INT32_MAX || I > INT32_MAX) return FP8MOT_ERR_INVALID_ARG;
+  // gate/up: K = H, FP8 output rows of I; down: K = I, BF16 output rows of H
+  if (!gemm_sizes_ok(M, I, H, I, 1) || !gemm_sizes_ok(M, H, I, H, 2)) return FP8MOT_ERR_INVALID_ARG;
   if (M == 0 || H == 0) return FP8MOT_OK;
   if (!x || !wg || !wu || !wd || !y) return FP8MOT_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(y))
@@ -278,6 +298,7 @@ int fp8_gate_up_swiglu(const uint8_t* qx, const uint8_t* wg, const float* d_sx,
   if (M < 0 || H < 0 || I < 0 || (H % 16) != 0 || (I % 16) != 0)
     return FP8MOT_ERR_INVALID_ARG;
   if (M > INT32_MAX || H > INT32_MAX || I > INT32_MAX) return FP8MOT_ERR_INVALID_ARG;
+  if (!gemm_sizes_ok(M, I, H, I, 1)) return FP8MOT_ERR_INVALID_ARG;
   if (M == 0 || I == 0) return FP8MOT_OK;
   if (!qh || (H > 0 && (!qx || !wg || !wu))) return FP8MOT_ERR_INVALID_ARG;
   if (!aligned16(qx) || !aligned16(wg) || !aligned16(wu) || !aligned16(qh))
@@ -304,6 +325,9 @@ int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
   if (M < 0 || H < 0 || Nq < 0 || Nk < 0 || Nv < 0 || (H % 16) != 0)
     return FP8MOT_ERR_INVALID_ARG;
   if (M > INT32_MAX || H > INT32_MAX || Nq > INT32_MAX || Nk > INT32_MAX || Nv > INT32_MAX)
+    return FP8MOT_ERR_INVALID_ARG;
+  // the grouped launch numbers the tiles of all three members together
+  if (!gemm_sizes_ok(M, Nq + Nk + Nv, H, Nq > Nk ? (Nq > Nv ? Nq : Nv) : (Nk > Nv ? Nk : Nv), 2))
     return FP8MOT_ERR_INVALID_ARG;
   if (M == 0) return FP8MOT_OK;
   // a member with N == 0 has nothing to read or write (its pointers may be NULL)

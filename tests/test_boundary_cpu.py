@@ -114,6 +114,25 @@ def test_refusals_before_any_device_access():
     assert lib.fp8_gate_up_swiglu(fake, fake, s, s, fake, s, s, fake, 4, 24, 16, 0, null) == 1
     assert lib.fp8_gate_up_swiglu(fake, odd, s, s, fake, s, s, fake, 4, 32, 16, 0, null) == 2
     assert lib.fp8_gate_up_swiglu(null, null, s, s, null, s, s, null, 0, 32, 16, 0, null) == 0
+    # sizes beyond the GEMM kernels' 32-bit tile windows -> INVALID_ARG
+    # (256 rows of K codes, 256 output rows of N or ldc elements)
+    kmax = 8388576                           # largest K (multiple of 16) with 256 * K < 0x7FFFF000
+    assert lib.fp8_linear(null, null, null, 0, 4, kmax + 16, s, s, 0, null, 0, null) == 1
+    assert lib.fp8_linear(null, null, null, 0, 4, kmax, s, s, 0, null, 0, null) == 0
+    nmax_bf16 = 0x7FFFF000 // (256 * 2) - 1  # BF16 output rows
+    assert lib.fp8_linear(null, null, null, 0, nmax_bf16 + 1, 16, s, s, 0, null, 0, null) == 1
+    assert lib.fp8_linear(null, null, null, 0, nmax_bf16, 16, s, s, 0, null, 0, null) == 0
+    # the same N fits FP8 output rows but not FP32 ones
+    assert lib.fp8_linear(null, null, null, 0, nmax_bf16 + 1, 16, s, s, 1, s, 0, null) == 0
+    assert lib.fp8_linear(null, null, null, 0, nmax_bf16 + 1, 16, s, s, 2, null, 0, null) == 1
+    assert lib.fp8_linear_ldc(null, null, null, 0, 32, 16, nmax_bf16 + 1, s, s, 0, null, 0, null) == 1
+    assert lib.fp8_gate_up_swiglu(null, null, s, s, null, s, s, null, 0, 32, kmax + 16, 0, null) == 1
+    assert lib.gated_mlp_fp8(null, 0, 16, kmax + 16, s, null, s, null, s, s, null, s,
+                             null, null, 0, 0, null) == 1
+    assert lib.qkv_fp8(null, 0, kmax + 16, s, null, 0, s, null, 0, s, null, 0, s,
+                       null, null, null, null, 0, 0, null) == 1
+    assert lib.qkv_fp8(null, 0, 16, s, null, nmax_bf16 + 1, s, null, 0, s, null, 0, s,
+                       null, null, null, null, 0, 0, null) == 1
     # unknown accumulation engine -> INVALID_ARG
     assert lib.fp8_linear(fake, fake, fake, 4, 4, 16, s, s, 0, null, 2, null) == 1
     assert lib.gated_mlp_fp8(fake, 4, 16, 32, s, fake, s, fake, s, s, fake, s,
