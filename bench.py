@@ -201,6 +201,7 @@ def main():
     rowwise = None if args.no_large else per_row_fp8(fp8, torch, dev, stream, M, H, I)
     topology = None if args.no_large else fused_topology(fp8, torch, dev, stream, qx, sx, sh, q, s)
     big_mlp = None if args.no_large else large_mlp(fp8, torch, dev, stream)
+    towers = None if args.no_large else two_tower_layer(fp8, torch, dev, stream)
 
     if args.copy_calib_mb > 0:
         n = args.copy_calib_mb << 20
@@ -227,6 +228,7 @@ def main():
         "per_row_fp8": rowwise,
         "fused_topology": topology,
         "large_mlp": big_mlp,
+        "two_tower_layer": towers,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out))
@@ -405,6 +407,98 @@ def large_mlp(fp8, torch, dev, stream):
             "peak_TFLOP/s": peak,
         }
     del x, qx, qh, y, ws, q
+    torch.cuda.empty_cache()
+    return out
+
+
+def two_tower_layer(fp8, torch, dev, stream):
+    """One decoder layer's FP8 Linear set for both towers (H=4096, I=12288;
+    und M=512 tokens, gen M=4096): per tower qkv_fp8 (one quantization, three
+    GEMMs), the o projection (its own quantize + GEMM) and gated_mlp_fp8.
+    Weights N(0, 0.02) RTN per tensor on the GPU; the layer's activations are
+    drawn N(0, 1) with 0.5% x20 outliers (attention itself is not on this
+    path, so the o-projection input is drawn too); input scales are each
+    site's amax/448 from the library's max observer on that input, down's
+    from fp8_observe_swiglu.  Average time of the whole set, both engines."""
+    H, I = 4096, 12288
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+
+    def act(M):
+        xf = torch.randn((M, H), device=dev, generator=gen)
+        xf = torch.where(torch.rand((M, H), device=dev, generator=gen) < 0.005, xf * 20, xf)
+        return xf.to(torch.bfloat16)
+
+    def weight(n, k):
+        return fp8.rtn_weight((torch.randn((n, k), device=dev, generator=gen) * 0.02)
+                              .to(torch.bfloat16))
+
+    def scale_of(x):
+        st = fp8.new_observer_state(dev)
+        fp8.fp8_observe(x, st, fp8.OBS_MAX)
+        return fp8.fp8_scale_from_state(st)
+
+    towers = {}
+    for name, M in (("und", 512), ("gen", 4096)):
+        t = {"M": M, "x_qkv": act(M), "x_o": act(M), "x_mlp": act(M)}
+        for k, (n, kk) in {"q": (H, H), "k": (H, H), "v": (H, H), "o": (H, H),
+                           "gate": (I, H), "up": (I, H), "down": (H, I)}.items():
+            t["w_" + k], t["s_" + k] = weight(n, kk)
+        t["sx_qkv"], t["sx_o"], t["sx_mlp"] = (scale_of(t["x_qkv"]), scale_of(t["x_o"]),
+                                              scale_of(t["x_mlp"]))
+        qx = fp8.fp8_quant_static(t["x_mlp"], t["sx_mlp"])
+        G = fp8.fp8_linear(qx, t["w_gate"], t["sx_mlp"], t["s_gate"])
+        U = fp8.fp8_linear(qx, t["w_up"], t["sx_mlp"], t["s_up"])
+        sth = fp8.new_observer_state(dev)
+        fp8.fp8_observe_swiglu(G, U, sth, fp8.OBS_MAX)
+        t["sh"] = fp8.fp8_scale_from_state(sth)
+        del qx, G, U
+        t["outs"] = tuple(torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in range(3))
+        t["ws_qkv"] = torch.empty(fp8.qkv_fp8_workspace(M, H), dtype=torch.uint8, device=dev)
+        t["qo"] = torch.empty((M, H), dtype=torch.uint8, device=dev)
+        t["yo"] = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        t["ws_mlp"] = torch.empty(fp8.gated_mlp_fp8_workspace(M, H, I), dtype=torch.uint8,
+                                  device=dev)
+        t["y"] = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        t["flops"] = 2.0 * M * H * H * 4 + 3 * 2.0 * M * I * H
+        towers[name] = t
+
+    def layer(t, acc):
+        fp8.qkv_fp8(t["x_qkv"], t["sx_qkv"], t["w_q"], t["s_q"], t["w_k"], t["s_k"],
+                    t["w_v"], t["s_v"], outs=t["outs"], workspace=t["ws_qkv"], accum=acc)
+        fp8.fp8_quant_static(t["x_o"], t["sx_o"], out=t["qo"])
+        fp8.fp8_linear(t["qo"], t["w_o"], t["sx_o"], t["s_o"], out=t["yo"], accum=acc)
+        fp8.gated_mlp_fp8(t["x_mlp"], t["sx_mlp"], t["w_gate"], t["s_gate"], t["w_up"],
+                          t["s_up"], t["sh"], t["w_down"], t["s_down"], out=t["y"],
+                          workspace=t["ws_mlp"], accum=acc)
+
+    def timed(f, reps=20):
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {"workload": "two_tower_layer_H4096_I12288_und512_gen4096",
+           "gemm_flops": {k: t["flops"] for k, t in towers.items()}}
+    for en, acc, peak in (("exact", fp8.ACC_EXACT, F16_PEAK_TFLOPS),
+                          ("fp8_mfma", fp8.ACC_FP8_MFMA, FP8_PEAK_TFLOPS)):
+        r = {}
+        for k, t in towers.items():
+            us = timed(lambda: layer(t, acc))
+            r[k] = {"us": us, "TFLOP/s": t["flops"] / (us * 1e-6) / 1e12}
+        us = timed(lambda: [layer(t, acc) for t in towers.values()])
+        tot = sum(t["flops"] for t in towers.values())
+        r["both_towers"] = {"us": us, "TFLOP/s": tot / (us * 1e-6) / 1e12,
+                            "frac_peak": tot / (us * 1e-6) / 1e12 / peak}
+        out[en] = r
+    del towers
     torch.cuda.empty_cache()
     return out
 
