@@ -104,13 +104,15 @@ typedef enum {
 
 /* Observer state, 16 bytes in device memory.  An all-zero state is a fresh
  * observer (the caller zero-fills it once).  `m` is the observed value,
- * `count` the number of calls folded in; `pending` is the library's own
- * reduction slot and is back at zero after each call; `reserved` stays 0. */
+ * `count` the number of calls folded in; `pending` (the call's running amax)
+ * and `arrived` (the call's workgroups that have added theirs) are the
+ * library's own reduction slots and are back at zero after each call.  Calls
+ * on one state must not overlap (use one stream, or one state per stream). */
 typedef struct {
   float m;
   int32_t count;
   uint32_t pending;
-  uint32_t reserved;
+  uint32_t arrived;
 } fp8mot_observer_state;
 
 /* ------------------------------------------------------------------ */

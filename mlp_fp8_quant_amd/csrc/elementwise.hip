@@ -316,11 +316,50 @@ __device__ __forceinline__ void block_max_to(uint32_t v, uint32_t* dst) {
   }
 }
 
+// Folds the call's amax (st->pending) into the state and clears the slot:
+// the first call sets m, later calls take the max (NaN sticks) or the moving
+// average m + c * (a - m) in three separately rounded FP32 operations.
+__device__ __forceinline__ void observer_fold(fp8mot_observer_state_dev* st, int mode, float c) {
+  const float a = __uint_as_float(
+      __hip_atomic_load(&st->pending, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  float m = st->m;
+  const int32_t count = st->count;
+  if (count == 0) {
+    m = a;
+  } else if (mode == 0) {
+    m = (a != a || m != m) ? __builtin_nanf("") : (a > m ? a : m);
+  } else {
+    const float d = __fsub_rn(a, m);
+    const float p = __fmul_rn(c, d);
+    m = __fadd_rn(m, p);
+  }
+  st->m = m;
+  st->count = count + 1;
+  st->pending = 0u;
+  st->arrived = 0u;
+}
+
+// End of an amax workgroup when the fold happens in the same launch: after
+// its atomic max, each workgroup counts itself in (release); the last one to
+// arrive (acquire) sees every workgroup's max and folds it into the state.
+__device__ __forceinline__ void arrive_and_fold(fp8mot_observer_state_dev* st, int mode, float c) {
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(&st->arrived, 1u);
+    if (prev == gridDim.x - 1) {
+      __threadfence();
+      observer_fold(st, mode, c);
+    }
+  }
+}
+
 // amax over BF16: max of (bits & 0x7FFF) as integers is max |x| exactly.
 // Sixteen 128-bit loads in flight per thread per step, so that a workgroup's
 // 32K-element share is one memory round trip rather than four.
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(
-    const uint16_t* __restrict__ x, int64_t n, uint32_t* __restrict__ pending) {
+    const uint16_t* __restrict__ x, int64_t n, fp8mot_observer_state_dev* st, int mode, float c,
+    int fold) {
+  uint32_t* pending = &st->pending;
   const int64_t units = n >> 3;                 // 8-element units
   constexpr int UN = 16;                        // units in flight per thread
   const int64_t stride = (int64_t)gridDim.x * kThreads * UN;
@@ -353,13 +392,15 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(
     }
   }
   block_max_to(m << 16, pending);
+  if (fold) arrive_and_fold(st, mode, c);
 }
 
 // amax of silu(g) * u in FP32 (as silu_mul_kernel evaluates it).  Four
 // 8-element units per thread per step.
 __global__ __launch_bounds__(kThreads) void amax_swiglu_kernel(
     const uint16_t* __restrict__ g, const uint16_t* __restrict__ u, int64_t n,
-    uint32_t* __restrict__ pending) {
+    fp8mot_observer_state_dev* st, int mode, float c, int fold) {
+  uint32_t* pending = &st->pending;
   const int64_t units = n >> 3;
   const int64_t stride = (int64_t)gridDim.x * kThreads * 4;
   const u32x4* gv = reinterpret_cast<const u32x4*>(g);
@@ -399,25 +440,13 @@ __global__ __launch_bounds__(kThreads) void amax_swiglu_kernel(
     }
   }
   block_max_to(m, pending);
+  if (fold) arrive_and_fold(st, mode, c);
 }
 
 // Folds the pending amax into the state and clears the slot.  One thread.
 __global__ void observer_update_kernel(fp8mot_observer_state_dev* st, int mode,
                                        float c) {
-  const float a = __uint_as_float(st->pending);
-  float m = st->m;
-  if (st->count == 0) {
-    m = a;
-  } else if (mode == 0) {
-    m = (a != a || m != m) ? __builtin_nanf("") : (a > m ? a : m);
-  } else {
-    const float d = __fsub_rn(a, m);
-    const float p = __fmul_rn(c, d);
-    m = __fadd_rn(m, p);
-  }
-  st->m = m;
-  st->count = st->count + 1;
-  st->pending = 0u;
+  observer_fold(st, mode, c);
 }
 
 __global__ void scale_from_state_kernel(const fp8mot_observer_state_dev* st,
@@ -498,21 +527,26 @@ hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,
   // 6.2 us and 512 take 8.6; for 52M, 512 take 17.8 us and 256 take 23.8).
   // With sixteen loads in flight per thread a workgroup's share is one memory
   // round trip: 4M elements 7.0 -> 4.1 us, 84M elements 26.8 us (6.3 TB/s).
-  // Folding the amax into the state in the last workgroup to finish, instead
-  // of the one-thread kernel below, was slower at both sizes: the arrival
-  // count is one more atomic per workgroup on one word.
   const int64_t want = (n + 32767) / 32768;
   const int cap = max_blocks / 4 > 0 ? max_blocks / 4 : 1;
   const int amax_blocks = want < 1 ? 1 : (want < cap ? (int)want : cap);
+  // Small grids fold the call's amax into the state in the last workgroup
+  // to finish; large ones in a second one-thread launch.  Each workgroup's
+  // release fence before its arrival count writes back its XCD's L2 (the 8
+  // XCDs' L2s are not coherent with one another), which is cheaper than a
+  // second launch for up to 128 workgroups (4M elements: 10.4 -> 7.6 us per
+  // call) and far dearer for 512 (84M elements: 28.5 -> 54.3 us).
+  const int64_t blocks = u == nullptr ? grid_for(n >> 7, amax_blocks) : grid_for(n >> 5, amax_blocks);
+  const int fold = blocks <= 128;
   if (u == nullptr) {
-    hipLaunchKernelGGL(amax_bf16_kernel, dim3(grid_for(n >> 7, amax_blocks)),
-                       dim3(kThreads), 0, stream, x, n, &st->pending);
+    hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       x, n, st, mode, c, fold);
   } else {
-    hipLaunchKernelGGL(amax_swiglu_kernel, dim3(grid_for(n >> 5, amax_blocks)),
-                       dim3(kThreads), 0, stream, x, u, n, &st->pending);
+    hipLaunchKernelGGL(amax_swiglu_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       x, u, n, st, mode, c, fold);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || fold) return e;
   hipLaunchKernelGGL(observer_update_kernel, dim3(1), dim3(1), 0, stream, st, mode, c);
   return hipGetLastError();
 }

@@ -13,7 +13,7 @@ struct fp8mot_observer_state_dev {
   float m;
   int32_t count;
   uint32_t pending;   // FP32 bit pattern of the running amax of the current call
-  uint32_t reserved;
+  uint32_t arrived;   // workgroups of the current call that have added their max
 };
 
 hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
