@@ -53,7 +53,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for {args.gpus}); "
               "the path has no multi-GPU code", file=sys.stderr)
         sys.exit(2)
 

@@ -7,7 +7,7 @@ not spell out the bit format; this oracle takes the OCP E4M3FN definition
 magnitude 448), which is the format whose maximum the workload descriptions
 state (448).
 
-Readings where the pages are silent (listed in the design doc as well):
+Readings where the pages are silent:
 
 * rounding is to nearest, ties to the even code (the card says "RTN" and
   "compress rounding" without a tie rule);

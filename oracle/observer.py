@@ -2,7 +2,7 @@
 
 Model card "Cosmos3-Nano-Policy-DROID, FP8 + RTN ...": the plain RTN build
 takes each static input scale from the global max of the activations seen
-during calibration; this build instead keeps a moving average of the per-call
+during calibration; the card's checkpoint instead keeps a moving average of the per-call
 maxima (MOVING_AVERAGE_MINMAX, averaging constant 0.01), which clips the
 rarest activations (header paragraph and section "Scheme").  Calibration ran
 256 transformer calls.
