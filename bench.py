@@ -164,7 +164,9 @@ def main():
 
     kernels = {
         "quant": {"us": us["quant"], "GB/s": quant_bytes / us["quant"] / 1e3,
-                  "bytes": quant_bytes},
+                  "bytes": quant_bytes,
+                  "note": "12 MB per launch: bound by launch and one memory round trip, not by "
+                          "bandwidth; elementwise_large.quant_16384x5120 is the HBM-bound size"},
         "gate_up_swiglu": {"us": us["gate_up_swiglu"], "flops": fused_flops,
                            "TFLOP/s": tflops(fused_flops, us["gate_up_swiglu"])},
         "down": {"us": us["down"], "flops": gate_flops,
