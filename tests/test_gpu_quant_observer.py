@@ -228,3 +228,42 @@ def test_refusals():
     with pytest.raises(fp8.Fp8motError) as e:
         fp8.fp8_quant_static(xb, scalar(1.0, dev))
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("mode", [fp8.OBS_MAX, fp8.OBS_MOVING_AVG])
+@pytest.mark.parametrize("n", [1 << 20, 8 << 20])
+def test_observer_in_hip_graph_folds_every_replay(mode, n):
+    # 1M elements fold in the amax launch itself (last workgroup to arrive),
+    # 8M in a second one-thread launch; either way a captured observe folds on
+    # every replay and leaves both reduction slots at zero, with eager calls
+    # on the same state between replays
+    dev = device()
+    rng = np.random.default_rng(n + mode)
+    draws = [workloads.to_bf16_bits(rng.standard_normal(n).astype(np.float32)
+                                    * np.float32(rng.uniform(0.5, 40))) for _ in range(6)]
+    st = fp8.new_observer_state(dev)
+    ost = oobs.ObserverState()
+    x_static = to_dev_bf16(draws[0], dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        warm = fp8.new_observer_state(dev)
+        fp8.fp8_observe(x_static, warm, mode)      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp8.fp8_observe(x_static, st, mode)
+    torch.cuda.synchronize()
+    assert st.cpu().numpy().tolist() == [0, 0, 0, 0]   # capture ran nothing
+    for t, bits in enumerate(draws):
+        if t % 2 == 0:
+            x_static.copy_(to_dev_bf16(bits, dev))
+            g.replay()
+        else:
+            fp8.fp8_observe(to_dev_bf16(bits, dev), st, mode)
+        torch.cuda.synchronize()
+        oobs.observe(ost, oobs.call_amax(bits), mode)
+        a = st.cpu().numpy()
+        assert a[:1].view(np.float32)[0].view(np.uint32) == np.float32(ost.m).view(np.uint32), t
+        assert int(a[1]) == t + 1 and int(a[2]) == 0 and int(a[3]) == 0, (t, a.tolist())
