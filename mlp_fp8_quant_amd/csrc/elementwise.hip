@@ -467,7 +467,9 @@ int grid_for(int64_t units, int max_blocks) {
 hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                                const float* d_scale, int max_blocks,
                                hipStream_t stream) {
-  hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(n >> 6, 2 * max_blocks)),
+  // up to 32 workgroups per CU, so that the large-MLP activation (84M
+  // elements) is one step of the grid: 49.5 -> 47.8 us against 16 per CU
+  hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(n >> 6, 4 * max_blocks)),
                      dim3(kThreads), 0, stream, x, q, n, d_scale);
   return hipGetLastError();
 }
