@@ -207,20 +207,34 @@ __global__ __launch_bounds__(kThreads) void quant_per_row_kernel(
     o.w = e4m3_pack4(f[12], f[13], f[14], f[15]);
     return o;
   };
+  // UH > 0: the next row's loads are issued before this row is reduced and
+  // encoded, so one row's memory round trip overlaps another's arithmetic
+  u32x4 hold[UH > 0 ? UH : 1][2], next[UH > 0 ? UH : 1][2];
+  auto load_row = [&](u32x4 (*dst)[2], int64_t r) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + r * K);
+#pragma unroll
+    for (int k = 0; k < UH; ++k) {
+      const int64_t i = threadIdx.x + k * kThreads;
+      if (i < units) {
+        dst[k][0] = __builtin_nontemporal_load(xr + 2 * i);
+        dst[k][1] = __builtin_nontemporal_load(xr + 2 * i + 1);
+      }
+    }
+  };
+  if constexpr (UH > 0) {
+    if (blockIdx.x < rows) load_row(next, blockIdx.x);
+  }
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     const u32x4* xr = reinterpret_cast<const u32x4*>(x + r * K);
     u32x4* qr = reinterpret_cast<u32x4*>(q + r * K);
     uint32_t m = 0;
-    u32x4 hold[UH > 0 ? UH : 1][2];
     if constexpr (UH > 0) {
 #pragma unroll
       for (int k = 0; k < UH; ++k) {
-        const int64_t i = threadIdx.x + k * kThreads;
-        if (i < units) {
-          hold[k][0] = __builtin_nontemporal_load(xr + 2 * i);
-          hold[k][1] = __builtin_nontemporal_load(xr + 2 * i + 1);
-        }
+        hold[k][0] = next[k][0];
+        hold[k][1] = next[k][1];
       }
+      if (r + gridDim.x < rows) load_row(next, r + gridDim.x);
 #pragma unroll
       for (int k = 0; k < UH; ++k)
         if (threadIdx.x + k * kThreads < units) m = max16(m, hold[k][0], hold[k][1]);
