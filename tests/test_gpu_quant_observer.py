@@ -267,3 +267,24 @@ def test_observer_in_hip_graph_folds_every_replay(mode, n):
         a = st.cpu().numpy()
         assert a[:1].view(np.float32)[0].view(np.uint32) == np.float32(ost.m).view(np.uint32), t
         assert int(a[1]) == t + 1 and int(a[2]) == 0 and int(a[3]) == 0, (t, a.tolist())
+
+
+@pytest.mark.parametrize("mode", [fp8.OBS_MAX, fp8.OBS_MOVING_AVG])
+def test_observer_random_sizes_both_fold_paths(mode):
+    # 300 calls on one state with sizes from 1 to 9M elements, so that calls
+    # alternate between the in-launch fold (<= 128 workgroups) and the
+    # separate fold launch; the state checked against the oracle every call
+    dev = device()
+    rng = np.random.default_rng(40 + mode)
+    pool = workloads.to_bf16_bits(rng.standard_normal(9 << 20).astype(np.float32))
+    dpool = to_dev_bf16(pool, dev)
+    st = fp8.new_observer_state(dev)
+    ost = oobs.ObserverState()
+    for t in range(300):
+        n = int(rng.integers(1, 9 << 20)) if t % 3 else int(rng.integers(1, 1 << 16))
+        off = int(rng.integers(0, (9 << 20) - n + 1)) // 8 * 8
+        fp8.fp8_observe(dpool[off:off + n], st, mode)
+        oobs.observe(ost, oobs.call_amax(pool[off:off + n]), mode)
+        a = st.cpu().numpy()
+        assert a[:1].view(np.float32)[0].view(np.uint32) == np.float32(ost.m).view(np.uint32), (t, n)
+        assert int(a[1]) == t + 1 and int(a[2]) == 0 and int(a[3]) == 0, (t, n, a.tolist())
