@@ -1,0 +1,87 @@
+"""The seeded synthetic inputs follow the recipe they are documented with:
+shapes of each workload, BF16 bit patterns, determinism per seed, the
+activation and weight distributions, the 0.5% x20 outliers and the
+calibration spikes (Bernoulli(0.005) positions, U(5, 30) gains).  These are
+statistical checks with wide margins on fixed seeds."""
+
+import numpy as np
+import pytest
+
+from mlp_fp8_quant_amd import workloads
+from oracle.formats import bf16_to_f32
+
+
+def test_workload_shapes():
+    wl = workloads.single_linear()
+    assert wl.x.shape == (64, 512) and wl.weights["w"].shape == (512, 512)
+    wl = workloads.gen_tower_mlp()
+    assert wl.x.shape == (2048, 2048)
+    assert wl.weights["gate"].shape == wl.weights["up"].shape == (8192, 2048)
+    assert wl.weights["down"].shape == (2048, 8192)
+    wl = workloads.split_qkv()
+    assert wl.x.shape == (3072, 4096)
+    assert all(w.shape == (4096, 4096) for w in wl.weights.values())
+    for tower, m in workloads.TOWER_M.items():
+        ws = workloads.layer_weights(tower)
+        assert {k: v.shape for k, v in ws.items()} == workloads.PROJ_SHAPES
+        assert workloads.forward_input(tower, "down").shape == (m, workloads.LAYER_I)
+    for wl in (workloads.gen_tower_mlp(), workloads.split_qkv()):
+        for a in (wl.x, *wl.weights.values()):
+            assert a.dtype == np.uint16 and a.flags["C_CONTIGUOUS"]
+
+
+def test_deterministic_per_seed_and_seed_sensitive():
+    a, b = workloads.gated_mlp(3, 64, 128, 256), workloads.gated_mlp(3, 64, 128, 256)
+    c = workloads.gated_mlp(4, 64, 128, 256)
+    assert np.array_equal(a.x, b.x) and np.array_equal(a.weights["down"], b.weights["down"])
+    assert not np.array_equal(a.x, c.x)
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -2.5, 0.0, -0.0], np.float32)
+    bits = workloads.to_bf16_bits(x)
+    # ties go to the even mantissa: 1 + 2^-8 -> 1, 1 + 3*2^-8 -> 1 + 2^-6
+    assert bits.tolist() == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x0000, 0x8000]
+
+
+def test_activation_outliers_and_weight_spread():
+    wl = workloads.gen_tower_mlp()
+    x = bf16_to_f32(wl.x).astype(np.float64)
+    # without outliers |x| > 5 has probability ~6e-7; an outlier is 20 z, so
+    # the share beyond 5 is ~0.005 * P(|z| > 0.25) = 0.0040
+    frac = np.mean(np.abs(x) > 5.0)
+    assert 0.0036 < frac < 0.0044, frac
+    inl = x[np.abs(x) <= 5.0]
+    assert abs(inl.mean()) < 0.01 and abs(inl.std() - 1.0) < 0.02
+    for k, w in wl.weights.items():
+        s = bf16_to_f32(w).astype(np.float64).std()
+        assert abs(s / 0.02 - 1.0) < 0.01, (k, s)
+    qkv = workloads.split_qkv()
+    assert np.max(np.abs(bf16_to_f32(qkv.x))) < 7.0     # no outliers there
+    sup = workloads.weights(np.random.default_rng(0), 512, 512, 0.015)
+    assert abs(bf16_to_f32(sup).astype(np.float64).std() / 0.015 - 1.0) < 0.02
+
+
+@pytest.mark.parametrize("tower", ["und", "gen"])
+def test_calibration_spikes(tower):
+    n = workloads.TOWER_M[tower] * workloads.LAYER_H
+    counts, gains = [], []
+    for t in range(64):
+        pos, gain = workloads.calib_spikes(tower, "qkv", t, n)
+        assert pos.min() >= 0 and pos.max() < n
+        counts.append(pos.size)
+        gains.append(float(gain))
+    mean = np.mean(counts) / n
+    assert abs(mean / workloads.OUTLIER_P - 1.0) < 0.05, mean
+    assert 5.0 <= min(gains) and max(gains) <= 30.0 and np.std(gains) > 4.0
+    # one call: the spiked positions are the base values times the gain
+    base = workloads.calib_base(tower, "qkv")
+    pos, gain = workloads.calib_spikes(tower, "qkv", 0, base.size)
+    x = workloads.calib_call(base, pos, gain)
+    f0, f1 = bf16_to_f32(base).ravel(), bf16_to_f32(x).ravel()
+    p = pos[:100]
+    want = bf16_to_f32(workloads.to_bf16_bits(f0[p] * np.float32(gain)))
+    assert np.array_equal(f1[p], want)
+    untouched = np.ones(base.size, bool)
+    untouched[pos] = False
+    assert np.array_equal(f0[untouched], f1[untouched])
