@@ -227,6 +227,11 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
         "fp8_mfma_engine": fp8_engine,
         "elementwise_large": large,
+        "roofline_hbm": None if large is None else [
+            {"kernel": k, "bound": "hbm", "achieved": large[k]["GB/s"], "peak": HBM_PEAK_GBS,
+             "unit": "GB/s", "frac": large[k]["GB/s"] / HBM_PEAK_GBS,
+             "bytes_per_launch": large[k]["bytes"], "traffic": None}
+            for k in ("quant_16384x5120", "silu_16384x25600")],
         "per_row_fp8": rowwise,
         "fused_topology": topology,
         "large_mlp": big_mlp,
