@@ -34,6 +34,23 @@ F16_PEAK_TFLOPS = 2500.0      # MI355X dense F16/BF16 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 
 
+def time_launches(torch, stream, f, reps, warm=2):
+    """Average time in microseconds of `reps` back-to-back calls f(r), r the
+    repetition index, after `warm` untimed calls: one pair of HIP events on
+    `stream` around the timed calls, no host synchronization between them."""
+    for r in range(warm):
+        f(r)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        f(r)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -137,19 +154,8 @@ def main():
             "silu": lambda: fp8.silu_mul_2in_fp8(Gb, Ub, sh, out=qh),
             "down": lambda: fp8.fp8_linear(qh, q["down"], sh, s["down"], out=y, accum=accum),
         }
-        out = {}
-        for n in names:
-            for _ in range(3):
-                calls[n]()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                calls[n]()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            out[n] = e0.elapsed_time(e1) / reps * 1e3
-        return out
+        return {n: time_launches(torch, stream, lambda r, c=calls[n]: c(), reps, warm=3)
+                for n in names}
 
     us = per_kernel(fp8.ACC_EXACT)
     us8 = per_kernel(fp8.ACC_FP8_MFMA)
@@ -253,17 +259,7 @@ def fused_topology(fp8, torch, dev, stream, qx, sx, sh, q, s):
     against one [3072, 12288] GEMM.  Also the share of codes the
     re-quantization changed (gate and up)."""
     def timed(f, reps=20):
-        for _ in range(2):
-            f()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            f()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
+        return time_launches(torch, stream, lambda r: f(), reps, warm=2)
 
     out = {}
     M, I = qx.shape[0], q["gate"].shape[0]
@@ -313,17 +309,7 @@ def per_row_fp8(fp8, torch, dev, stream, M, H, I):
     the large MLP's X [16384, 5120] (3 B per element), and the gate projection
     [M, I, H] with per-row scales on both engines (TFLOP/s)."""
     def timed(f, reps):
-        for r in range(2):
-            f(r)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for r in range(reps):
-            f(r)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
+        return time_launches(torch, stream, f, reps, warm=2)
 
     out = {}
     for rows, k, reps in ((M, H, 50), (16384, 5120, 20)):
@@ -361,16 +347,7 @@ def large_mlp(fp8, torch, dev, stream):
     gen.manual_seed(5)
 
     def timed(f, reps=4):
-        f()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            f()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
+        return time_launches(torch, stream, lambda r: f(), reps, warm=1)
 
     xf = torch.randn((M, H), device=dev, generator=gen)
     xf = torch.where(torch.rand((M, H), device=dev, generator=gen) < 0.005, xf * 20, xf)
@@ -480,17 +457,7 @@ def two_tower_layer(fp8, torch, dev, stream):
                           workspace=t["ws_mlp"], accum=acc)
 
     def timed(f, reps=20):
-        for _ in range(5):
-            f()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            f()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
+        return time_launches(torch, stream, lambda r: f(), reps, warm=5)
 
     out = {"workload": "two_tower_layer_H4096_I12288_und512_gen4096",
            "gemm_flops": {k: t["flops"] for k, t in towers.items()}}
@@ -518,17 +485,7 @@ def elementwise_large(fp8, torch, dev, stream):
     for quantize), algorithmic GB/s, and the fraction of the 8 TB/s peak.
     A plain device copy of the SwiGLU's byte count is timed beside them."""
     def timed(f, reps):
-        for r in range(2):
-            f(r)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for r in range(reps):
-            f(r)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
+        return time_launches(torch, stream, f, reps, warm=2)
 
     out = {}
     n = 16384 * 5120
