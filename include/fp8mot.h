@@ -23,7 +23,8 @@
  *  - Every scale is a `const float*` DEVICE pointer to one FP32 scalar.  The
  *    library never reads a scale on the host: a host read would synchronize
  *    the device on the hot path ([PR] "What changed": the shared-scale
- *    invariant is checked at load, never in forward).  A NULL scale asks for
+ *    invariant is validated once when the weights are loaded, and no scale
+ *    is read during the forward pass).  A NULL scale asks for
  *    dynamic quantization, which the static path refuses
  *    (FP8MOT_ERR_UNSUPPORTED; [PR] "What changed": dynamic quantization is
  *    rejected explicitly).
@@ -34,7 +35,8 @@
  *    launched when a call returns an error.
  *  - Base pointers of tensors must be 16-byte aligned (128-bit loads and
  *    stores); otherwise FP8MOT_ERR_MISALIGNED -- a refusal, not a slow path
- *    ([PR] "Supported surface": a quiet fallback is worse than a refusal).
+ *    ([PR] "Supported surface, and what is refused": an unsupported case is
+ *    refused outright rather than served by a silent fallback).
  *  - Sizes are int64_t element counts.  Negative sizes are
  *    FP8MOT_ERR_INVALID_ARG; an empty tensor (a zero size) is a valid no-op
  *    and then data pointers may be NULL.
@@ -350,7 +352,8 @@ int fp8_scale_from_state(const void* d_state, float* d_scale,
 
 /* Load-time check of a shared-quantization group ([PR] "What changed": the
  * projections sharing one quantized activation must carry the same
- * calibrated input_scale; checked at load, never in forward).
+ * calibrated input_scale; validated when the weights are loaded, not in the
+ * forward pass).
  * h_scales: HOST array of n >= 1 scales.  FP8MOT_OK iff all are finite,
  * > 0 and bitwise equal; FP8MOT_ERR_SCALE_MISMATCH if they differ;
  * FP8MOT_ERR_INVALID_ARG for NULL, n < 1, or a non-finite or non-positive

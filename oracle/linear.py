@@ -119,17 +119,6 @@ def epilogue_fp8(S, s_x, s_w, s_y) -> np.ndarray:
         return e4m3_encode(y32 / np.float32(s_y))
 
 
-def linear_bf16(x_bf16, s_x, qw, s_w):
-    """Whole static FP8 Linear: quantize X, exact GEMM, BF16 epilogue.
-
-    Returns (y_bf16_bits, y32, qx, S, A).
-    """
-    qx = quant_static(x_bf16, s_x)
-    S, A = gemm_exact(qx, qw)
-    y32 = epilogue_f32(S, s_x, s_w)
-    return f32_to_bf16(y32), y32, qx, S, A
-
-
 def requantize_onto_max(qws, scales):
     """Failure mode of a fused group holding one scale (negative reference).
 
@@ -150,8 +139,9 @@ def check_shared_scale(scales) -> bool:
     """Load-time invariant of a shared-quantization group.
 
     Pull request section "What changed": the projections of a group must
-    carry the same calibrated input_scale; this is checked at load, never in
-    forward.  True iff every scale is finite, > 0 and all are bitwise equal.
+    carry the same calibrated input_scale, validated once when the weights
+    are loaded and not in the forward pass.  True iff every scale is finite,
+    > 0 and all are bitwise equal.
     """
     s = np.asarray(scales, dtype=np.float32)
     if s.size == 0:

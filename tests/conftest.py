@@ -12,9 +12,6 @@ def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
-
-def pytest_collection_modifyitems(config, items):
-    # A GPU test must never pass by skipping: on a host without a GPU the
+    # A GPU test never passes by skipping: on a host without a GPU the
     # gpu-marked tests are deselected with -m "not gpu"; run with -m gpu they
-    # fail loudly if no device is present (see tests/gpu_common.py).
-    pass
+    # fail loudly when no device is present (gpu_util.device()).

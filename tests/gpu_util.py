@@ -12,6 +12,9 @@ Tolerances (stated where the checks are made):
   most 0.1% of the elements.
 """
 
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -23,6 +26,17 @@ def device():
     if not torch.cuda.is_available():
         pytest.fail("a gpu-marked test ran without a visible GPU")
     return torch.device("cuda:0")
+
+
+def report(key, value):
+    """Records a measured figure of a parity test (a count or a fraction):
+    printed, and appended as one JSON line to the file named by the
+    FP8MOT_REPORT environment variable when it is set."""
+    print(f"[report] {key} = {value}", flush=True)
+    path = os.environ.get("FP8MOT_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"key": key, "value": value}) + "\n")
 
 
 def to_dev_bf16(bits, dev):

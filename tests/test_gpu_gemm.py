@@ -17,7 +17,7 @@ from oracle.formats import (E4M3_TABLE, bf16_ulps, e4m3_decode, e4m3_encode,
 
 from gpu_util import (check_fp8_tolerance, check_gemm_bf16, check_gemm_f32,
                       check_gemm_fp8_engine, device, fp8_mfma_group_bound,
-                      host_bits, host_f32, host_u8, scalar, to_dev_u8)
+                      host_bits, host_f32, host_u8, report, scalar, to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,8 +152,10 @@ def test_fp8_output_is_the_encoded_f32_output(accum, M, N, K):
     assert np.array_equal(host_u8(out[fp8.OUT_FP8]), want)
 
 
-def _linear_case(x_bits, w_bits, dev, rows=None, accum=fp8.ACC_EXACT):
-    """Quantize x and w as the method does and compare one projection."""
+def _linear_case(x_bits, w_bits, dev, rows=None, accum=fp8.ACC_EXACT, key=None):
+    """Quantize x and w as the method does and compare one projection;
+    `key` names the figures reported (the outputs that needed R-13's second
+    clause, or the FP8 engine's share beyond 1e-5 sum|terms|)."""
     sx = olin.scale_from_amax(olin.amax_f32(x_bits))
     qx = olin.quant_static(x_bits, sx)
     qw, sw = olin.rtn_weight(w_bits)
@@ -166,11 +168,15 @@ def _linear_case(x_bits, w_bits, dev, rows=None, accum=fp8.ACC_EXACT):
     alpha = olin.epilogue_alpha(sx, sw)
     if accum == fp8.ACC_EXACT:
         check_gemm_f32(y32, S, A, alpha)
-        return check_gemm_bf16(yb, y32, S, A, alpha)
+        n2 = check_gemm_bf16(yb, y32, S, A, alpha)
+        if key:
+            report(f"{key}_r13_second_clause", n2)
+        return n2
     sub = slice(0, 16)  # the group bound is costly; evaluate it on 16 rows
     frac = check_gemm_fp8_engine(y32[sub], S[sub], A[sub], alpha,
                                  fp8_mfma_group_bound(qx[sub], qw))
-    print(f"fp8 engine: {frac:.4%} of sampled outputs beyond 1e-5 sum|terms|")
+    if key:
+        report(f"{key}_fp8_engine_frac_beyond_1e-5", frac)
     return frac
 
 
@@ -178,7 +184,7 @@ def _linear_case(x_bits, w_bits, dev, rows=None, accum=fp8.ACC_EXACT):
 def test_single_linear_config(accum):
     dev = device()
     wl = workloads.single_linear()
-    _linear_case(wl.x, wl.weights["w"], dev, accum=accum)
+    _linear_case(wl.x, wl.weights["w"], dev, accum=accum, key="single_linear_64x512x512")
 
 
 @pytest.mark.parametrize("accum", ENGINES)
@@ -186,18 +192,19 @@ def test_gen_mlp_gate_up_down_shapes(accum):
     dev = device()
     wl = workloads.gen_tower_mlp()
     for name in ("gate", "up"):
-        _linear_case(wl.x, wl.weights[name], dev, accum=accum)
+        _linear_case(wl.x, wl.weights[name], dev, accum=accum,
+                     key=f"gen_mlp_{name}_2048x8192x2048")
     # down: its input is the [2048, 8192] SwiGLU output; a draw of the same
     # shape stands in here (the chained case is in the composite tests)
     h = workloads.activations(np.random.default_rng(5), 2048, 8192)
-    _linear_case(h, wl.weights["down"], dev, accum=accum)
+    _linear_case(h, wl.weights["down"], dev, accum=accum, key="gen_mlp_down_2048x2048x8192")
 
 
 def test_split_qkv_shapes():
     dev = device()
     wl = workloads.split_qkv()
     for name in ("q", "k", "v"):
-        _linear_case(wl.x, wl.weights[name], dev)
+        _linear_case(wl.x, wl.weights[name], dev, key=f"split_qkv_{name}_3072x4096x4096")
 
 
 def test_two_tower_shapes_sampled_rows():
@@ -220,7 +227,7 @@ def test_super_mlp_shapes_sampled_rows():
     x = workloads.activations(rng, 16384, 5120)
     w = workloads.weights(rng, 25600, 5120, 0.015)
     rows = np.sort(np.random.default_rng(4).choice(16384, 64, replace=False))
-    _linear_case(x, w, dev, rows=rows)
+    _linear_case(x, w, dev, rows=rows, key="super_mlp_gate_16384x25600x5120_64rows")
 
 
 @pytest.mark.parametrize("accum", ENGINES)

@@ -12,8 +12,8 @@ from oracle.formats import e4m3_decode
 from oracle.swiglu import silu_mul_f64, silu_mul_fp8
 
 from gpu_util import (check_fp8_tolerance, check_gemm_bf16, check_gemm_f32,
-                      device, host_bits,
-                      host_u8, scalar, to_dev_bf16, to_dev_u8)
+                      device, host_bits, host_f32, host_u8, report, scalar,
+                      to_dev_bf16, to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,13 +111,16 @@ def test_gated_mlp_composite_equals_parts_and_oracle():
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(fp8.fp8_gate_up_swiglu(qx, c["d"]["gate"], dsx, c["sc"]["gate"],
                                               c["d"]["up"], c["sc"]["up"], dsh), qh)
-    # stage-wise against the oracle
+    # stage-wise against the oracle: qX bit-exact; G and U within 1 BF16 ulp
+    # of the oracle's (or, near cancellation, the RNE of an FP32 output
+    # within 1e-5 sum|terms|); the SwiGLU codes within one step on <= 0.1%
     assert np.array_equal(host_u8(qx), c["qx"])
-    Gb = host_bits(G)
-    nG = int(np.count_nonzero(Gb != c["G"]))
-    assert nG <= 1e-3 * Gb.size
-    check_fp8_tolerance(host_u8(qh).ravel(),
-                        silu_mul_fp8(c["G"], c["U"], c["sh"]))
+    for k, t, S_, A_ in (("gate", G, c["Sg"], c["Ag"]), ("up", U, c["Su"], c["Au"])):
+        t32 = host_f32(fp8.fp8_linear(qx, c["d"][k], dsx, c["sc"][k], fp8.OUT_F32))
+        n2 = check_gemm_bf16(host_bits(t), t32, S_, A_, olin.epilogue_alpha(c["sx"], c["s"][k]))
+        report(f"gen_mlp_{k}_2048x8192x2048_r13_second_clause", n2)
+    n_off = check_fp8_tolerance(host_u8(qh).ravel(), silu_mul_fp8(c["G"], c["U"], c["sh"]))
+    report("gen_mlp_swiglu_2048x8192_codes_one_step_off_frac", n_off / qh.numel())
     # end to end: the oracle chain, with the tolerance widened by exactly the
     # effect of the SwiGLU codes that differ by one step
     qh_o = silu_mul_fp8(c["G"], c["U"], c["sh"]).reshape(2048, 8192)
@@ -158,8 +161,9 @@ def test_qkv_composite_equals_parts_and_oracle():
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
         S, A = olin.gemm_exact(qx, qs[k])
         y32 = fp8.fp8_linear(dqx, d[k], dsx, sc[k], fp8.OUT_F32)
-        check_gemm_bf16(host_bits(y), y32.cpu().numpy(), S, A,
-                        olin.epilogue_alpha(sx, ss[k]))
+        n2 = check_gemm_bf16(host_bits(y), y32.cpu().numpy(), S, A,
+                             olin.epilogue_alpha(sx, ss[k]))
+        report(f"split_qkv_{k}_3072x4096x4096_r13_second_clause", n2)
 
 
 def test_split_path_keeps_each_members_codes_not_requantized():
