@@ -15,7 +15,8 @@
  * --------------------------------
  *  - All tensor pointers are DEVICE pointers on the current HIP device,
  *    owned by the caller; the library allocates nothing and keeps no
- *    per-call state.  Tensors are dense and contiguous (row-major); a
+ *    per-call state (the one exception is the fixed scratch array behind
+ *    gated_mlp_fp8_noalloc, see there).  Tensors are dense and contiguous (row-major); a
  *    strided tensor must be rejected by the caller before it gets here
  *    ([PR] first commit message: strided inputs are refused, not copied).
  *  - BF16 tensors are passed as uint16_t bit patterns, FP8 tensors as uint8_t
@@ -69,8 +70,13 @@ typedef enum {
   FP8MOT_ERR_SCALE_MISMATCH = 3, /* a shared-quantization group's input scales differ */
   FP8MOT_ERR_UNSUPPORTED = 4,    /* NULL scale (dynamic quantization) or non-gfx950 device */
   FP8MOT_ERR_HIP = 5,            /* a HIP runtime call or a kernel launch failed */
-  FP8MOT_ERR_WORKSPACE = 6       /* workspace NULL, misaligned or smaller than required */
+  FP8MOT_ERR_WORKSPACE = 6,      /* workspace NULL, misaligned or smaller than required */
+  FP8MOT_ERR_TOO_LARGE = 7       /* sizes exceed the allocation-free entry point's scratch */
 } fp8mot_status;
+
+/* Bytes of device scratch behind gated_mlp_fp8_noalloc (one copy per device,
+ * held by the library until the process ends). */
+#define FP8MOT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Output kind of fp8_linear. */
 typedef enum {
@@ -287,6 +293,26 @@ int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
                   const uint8_t* wu, const float* d_su, const float* d_sh,
                   const uint8_t* wd, const float* d_sd, uint16_t* y, void* ws,
                   size_t ws_bytes, int accum, hipStream_t stream);
+
+/* gated_mlp_fp8 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same launches and bitwise the same y, with qX and qH kept in a scratch
+ * array the library holds per device (FP8MOT_NOALLOC_SCRATCH_BYTES, a
+ * file-scope device array whose address is looked up once per device)
+ * instead of a caller workspace.  The call allocates nothing.
+ * Limit: gated_mlp_fp8_workspace(M, H, I) <= FP8MOT_NOALLOC_SCRATCH_BYTES
+ * (64 MiB: M * (H + I) up to about 64M codes, e.g. M = 4096, H = 4096,
+ * I = 12288), else FP8MOT_ERR_TOO_LARGE and nothing is launched.
+ * Every call on one device shares that device's scratch: calls that overlap
+ * on one GPU (different streams, or different threads without ordering) race
+ * on it and must be serialized by the caller.  Nothing in the scratch needs
+ * to start at zero (each call overwrites the qX and qH it reads).  Other
+ * arguments, refusals and the engine choice as gated_mlp_fp8. */
+int gated_mlp_fp8_noalloc(const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                          const float* d_sx, const uint8_t* wg, const float* d_sg,
+                          const uint8_t* wu, const float* d_su, const float* d_sh,
+                          const uint8_t* wd, const float* d_sd, uint16_t* y, int accum,
+                          hipStream_t stream);
 
 /* The gate/up half of the gated MLP from an already quantized activation
  * ([PR] "What changed": one quantized activation handed to both

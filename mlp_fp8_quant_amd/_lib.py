@@ -41,6 +41,9 @@ SIGNATURES = {
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_int, c_void_p]),
+    "gated_mlp_fp8_noalloc": (c_int, [c_void_p, c_i64, c_i64, c_i64, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
     "fp8_gate_up_swiglu": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64,
                                    c_int, c_void_p]),
@@ -59,7 +62,7 @@ SIGNATURES = {
 STATUS = {
     0: "FP8MOT_OK", 1: "FP8MOT_ERR_INVALID_ARG", 2: "FP8MOT_ERR_MISALIGNED",
     3: "FP8MOT_ERR_SCALE_MISMATCH", 4: "FP8MOT_ERR_UNSUPPORTED",
-    5: "FP8MOT_ERR_HIP", 6: "FP8MOT_ERR_WORKSPACE",
+    5: "FP8MOT_ERR_HIP", 6: "FP8MOT_ERR_WORKSPACE", 7: "FP8MOT_ERR_TOO_LARGE",
 }
 
 _lib = None

@@ -306,6 +306,33 @@ def gated_mlp_fp8(x, sx, wg, sg, wu, su, sh, wd, sd, out=None, workspace=None,
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20   # FP8MOT_NOALLOC_SCRATCH_BYTES
+
+
+def gated_mlp_fp8_noalloc(x, sx, wg, sg, wu, su, sh, wd, sd, out, accum=ACC_EXACT):
+    """gated_mlp_fp8 without a workspace: the library keeps qX and qH in its
+    own per-device scratch (at most NOALLOC_SCRATCH_BYTES); the caller passes
+    the output.  Calls that overlap on one GPU race on that scratch."""
+    _need(x, "x", torch.bfloat16)
+    dev = x.device
+    for t, n in ((wg, "wg"), (wu, "wu"), (wd, "wd")):
+        _need(t, n, torch.uint8, dev)
+    H = x.shape[-1]
+    I = wg.shape[0]
+    if wg.shape != (I, H) or wu.shape != (I, H) or wd.shape != (H, I):
+        raise ValueError("shapes: wg, wu [I, H]; wd [H, I]")
+    for t, n in ((sx, "sx"), (sg, "sg"), (su, "su"), (sh, "sh"), (sd, "sd")):
+        _scale(t, n, dev)
+    M = math.prod(x.shape[:-1])
+    _need(out, "out", torch.bfloat16, dev)
+    if out.numel() != M * H:
+        raise ValueError("out must hold M * H elements")
+    _lib.call("gated_mlp_fp8_noalloc", _ptr(x), M, H, I, _ptr(sx), _ptr(wg), _ptr(sg),
+              _ptr(wu), _ptr(su), _ptr(sh), _ptr(wd), _ptr(sd), _ptr(out), accum,
+              _stream(x))
+    return out
+
+
 def qkv_fp8_workspace(M, H):
     return int(_lib.lib().qkv_fp8_workspace(M, H))
 

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/fp8mot.h"
 #include "kernels.h"
@@ -122,6 +123,7 @@ const char* fp8mot_status_string(int status) {
     case FP8MOT_ERR_UNSUPPORTED: return "unsupported: NULL scale (dynamic quantization) or non-gfx950 device";
     case FP8MOT_ERR_HIP: return "HIP runtime error or kernel launch failure";
     case FP8MOT_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
+    case FP8MOT_ERR_TOO_LARGE: return "sizes need more scratch than the allocation-free entry point holds (FP8MOT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -253,11 +255,15 @@ size_t gated_mlp_fp8_workspace(int64_t M, int64_t H, int64_t I) {
   return mlp_layout(M, H, I).total;
 }
 
-int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
-                  const float* d_sx, const uint8_t* wg, const float* d_sg,
-                  const uint8_t* wu, const float* d_su, const float* d_sh,
-                  const uint8_t* wd, const float* d_sd, uint16_t* y, void* ws,
-                  size_t ws_bytes, int accum, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the gated MLP (everything but the workspace).
+int check_gated_mlp(const uint16_t* x, int64_t M, int64_t H, int64_t I, const float* d_sx,
+                    const uint8_t* wg, const float* d_sg, const uint8_t* wu,
+                    const float* d_su, const float* d_sh, const uint8_t* wd,
+                    const float* d_sd, const uint16_t* y, int accum) {
   if (!d_sx || !d_sg || !d_su || !d_sh || !d_sd) return FP8MOT_ERR_UNSUPPORTED;
   if (accum != FP8MOT_ACC_EXACT && accum != FP8MOT_ACC_FP8_MFMA) return FP8MOT_ERR_INVALID_ARG;
   if (M < 0 || H < 0 || I < 0 || (H % 16) != 0 || (I % 16) != 0)
@@ -269,24 +275,93 @@ int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
   if (!x || !wg || !wu || !wd || !y) return FP8MOT_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(y))
     return FP8MOT_ERR_MISALIGNED;
+  return FP8MOT_OK;
+}
+
+// The gated MLP's launches, with qX and qH in `base` laid out by mlp_layout.
+int run_gated_mlp(const uint16_t* x, int64_t M, int64_t H, int64_t I, const float* d_sx,
+                  const uint8_t* wg, const float* d_sg, const uint8_t* wu, const float* d_su,
+                  const float* d_sh, const uint8_t* wd, const float* d_sd, uint16_t* y,
+                  uint8_t* base, int accum, int cus, hipStream_t stream) {
   const MlpLayout l = mlp_layout(M, H, I);
-  if (ws == nullptr || !aligned256(ws) || ws_bytes < l.total) return FP8MOT_ERR_WORKSPACE;
-  int cus = 0;
-  int st = current_device(&cus);
-  if (st != FP8MOT_OK) return st;
-  uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* qx = base + l.qx;
   uint8_t* qh = base + l.qh;
   g_quant_launches.fetch_add(1);
   hipError_t e = launch_quant_static(x, qx, M * H, d_sx, ew_blocks(cus), stream);
   // gate and up GEMMs with the SwiGLU-FP8 epilogue in one launch: the same
   // arithmetic, in the same order, as the two BF16 GEMMs and
-  // silu_mul_2in_fp8, without writing G and U
+  // silu_mul_2in_fp8 whenever those GEMMs sum K in one running sum, without
+  // writing G and U
   if (e == hipSuccess && I > 0)
     e = launch_gemm_swiglu(qx, wg, wu, qh, M, I, H, d_sx, d_sg, d_su, d_sh, accum, stream);
   if (e == hipSuccess)
     e = launch_gemm(qh, wd, y, M, H, I, d_sh, d_sd, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
   return hip_status(e);
+}
+
+// Scratch of gated_mlp_fp8_noalloc: qX and qH at the offsets of
+// gated_mlp_fp8's workspace.  Each device the library runs on holds its own
+// copy until the process ends.  Host code never passes `scratch` itself (on
+// the host it names a stand-in, not device memory): it passes the device
+// address that hipGetSymbolAddress returns for the current device, taken once
+// per device and kept in g_scratch_dev.
+static __device__ __align__(256) uint8_t scratch[FP8MOT_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+// Device address of the current device's scratch (the caller has checked the
+// device: 0 <= dev < kMaxDevices and gfx950).
+int scratch_of_device(int dev, uint8_t** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return FP8MOT_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(g_scratch_dev[dev]);
+  return FP8MOT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                  const float* d_sx, const uint8_t* wg, const float* d_sg,
+                  const uint8_t* wu, const float* d_su, const float* d_sh,
+                  const uint8_t* wd, const float* d_sd, uint16_t* y, void* ws,
+                  size_t ws_bytes, int accum, hipStream_t stream) {
+  int st = check_gated_mlp(x, M, H, I, d_sx, wg, d_sg, wu, d_su, d_sh, wd, d_sd, y, accum);
+  if (st != FP8MOT_OK || M == 0 || H == 0) return st;
+  if (ws == nullptr || !aligned256(ws) || ws_bytes < mlp_layout(M, H, I).total)
+    return FP8MOT_ERR_WORKSPACE;
+  int cus = 0;
+  st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return run_gated_mlp(x, M, H, I, d_sx, wg, d_sg, wu, d_su, d_sh, wd, d_sd, y,
+                       static_cast<uint8_t*>(ws), accum, cus, stream);
+}
+
+int gated_mlp_fp8_noalloc(const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                          const float* d_sx, const uint8_t* wg, const float* d_sg,
+                          const uint8_t* wu, const float* d_su, const float* d_sh,
+                          const uint8_t* wd, const float* d_sd, uint16_t* y, int accum,
+                          hipStream_t stream) {
+  int st = check_gated_mlp(x, M, H, I, d_sx, wg, d_sg, wu, d_su, d_sh, wd, d_sd, y, accum);
+  if (st != FP8MOT_OK || M == 0 || H == 0) return st;
+  if (mlp_layout(M, H, I).total > FP8MOT_NOALLOC_SCRATCH_BYTES) return FP8MOT_ERR_TOO_LARGE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FP8MOT_ERR_HIP;
+  int cus = 0;
+  st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  uint8_t* base = nullptr;
+  st = scratch_of_device(dev, &base);
+  if (st != FP8MOT_OK) return st;
+  return run_gated_mlp(x, M, H, I, d_sx, wg, d_sg, wu, d_su, d_sh, wd, d_sd, y, base, accum,
+                       cus, stream);
 }
 
 int fp8_gate_up_swiglu(const uint8_t* qx, const uint8_t* wg, const float* d_sx,

@@ -46,8 +46,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib()
-    for st in range(7):
-        assert lib.fp8mot_status_string(st)
+    for st in range(8):
+        assert lib.fp8mot_status_string(st) != b"unknown status"
     assert lib.fp8mot_status_string(99) == b"unknown status"
 
 
@@ -133,6 +133,18 @@ def test_refusals_before_any_device_access():
                        null, null, null, null, 0, 0, null) == 1
     assert lib.qkv_fp8(null, 0, 16, s, null, nmax_bf16 + 1, s, null, 0, s, null, 0, s,
                        null, null, null, null, 0, 0, null) == 1
+    # the allocation-free gated MLP: the gated MLP's own refusals, and sizes
+    # whose qX + qH exceed its fixed 64 MiB scratch -> TOO_LARGE, all before
+    # any device access
+    na = lib.gated_mlp_fp8_noalloc
+    assert na(fake, 4, 16, 32, null, fake, s, fake, s, s, fake, s, fake, 0, null) == 4
+    assert na(fake, 4, 16, 24, s, fake, s, fake, s, s, fake, s, fake, 0, null) == 1
+    assert na(fake, 4, 16, 32, s, fake, s, fake, s, s, fake, s, fake, 3, null) == 1
+    assert na(fake, 4, 16, 32, s, odd, s, fake, s, s, fake, s, fake, 0, null) == 2
+    assert na(null, 0, 16, 32, s, null, s, null, s, s, null, s, null, 0, null) == 0
+    assert na(fake, 4097, 4096, 12288, s, fake, s, fake, s, s, fake, s, fake, 0, null) == 7
+    assert na(fake, 16384, 5120, 25600, s, fake, s, fake, s, s, fake, s, fake, 0, null) == 7
+    assert lib.gated_mlp_fp8_workspace(4096, 4096, 12288) == 64 << 20   # fits exactly
     # unknown accumulation engine -> INVALID_ARG
     assert lib.fp8_linear(fake, fake, fake, 4, 4, 16, s, s, 0, null, 2, null) == 1
     assert lib.gated_mlp_fp8(fake, 4, 16, 32, s, fake, s, fake, s, s, fake, s,
