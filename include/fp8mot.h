@@ -140,6 +140,16 @@ const char* fp8mot_status_string(int status);
  * the single-quantization property: a composite call adds exactly 1. */
 uint64_t fp8mot_debug_quant_launches(void);
 
+/* Measurement aid, not a step of the path: the read/write ceiling of the
+ * HBM-bound kernels' byte mix.  Reads a[0..n) (and b[0..n) when b is not
+ * NULL) as 16-bit words and writes out[0..n) = the low byte of a[i] (or of
+ * a[i] ^ b[i]): 2 bytes read + 1 written per element like fp8_quant_static,
+ * or 4 + 1 like silu_mul_2in_fp8, with their access pattern and grid and no
+ * arithmetic.  a, b: [n] 16-byte aligned; out: [n] 16-byte aligned.
+ * Refusals as fp8_quant_static (no scale). */
+int fp8mot_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_t n,
+                      hipStream_t stream);
+
 /* ------------------------------------------------------------------ */
 /* Steps of the hot path                                               */
 /* ------------------------------------------------------------------ */

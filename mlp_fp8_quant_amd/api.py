@@ -414,6 +414,22 @@ def fp8_check_shared_scale(scales):
     _lib.call("fp8_check_shared_scale", arr, n)
 
 
+def rw_ceiling(a, b, out):
+    """Measurement aid: the quantize (b None) or SwiGLU (b given) byte mix with
+    no arithmetic; out[i] = low byte of a[i] (^ b[i]).  a, b: 16-bit tensors
+    (any 2-byte dtype), out: uint8 with as many elements."""
+    if a.element_size() != 2 or (b is not None and b.element_size() != 2):
+        raise ValueError("a and b must hold 2-byte elements")
+    for t, n in ((a, "a"), (out, "out")) + (((b, "b"),) if b is not None else ()):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous GPU tensor")
+    if out.dtype != torch.uint8 or out.numel() != a.numel() or (
+            b is not None and b.numel() != a.numel()):
+        raise ValueError("out must be uint8 with as many elements as a (and b)")
+    _lib.call("fp8mot_rw_ceiling", _ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(a))
+    return out
+
+
 def debug_quant_launches():
     return int(_lib.lib().fp8mot_debug_quant_launches())
 

@@ -130,6 +130,19 @@ const char* fp8mot_status_string(int status) {
 
 uint64_t fp8mot_debug_quant_launches(void) { return g_quant_launches.load(); }
 
+int fp8mot_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_t n,
+                      hipStream_t stream) {
+  if (n < 0) return FP8MOT_ERR_INVALID_ARG;
+  if (n == 0) return FP8MOT_OK;
+  if (a == nullptr || out == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(out) || (b != nullptr && !aligned16(b)))
+    return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_rw_ceiling(a, b, out, n, ew_blocks(cus), stream));
+}
+
 int fp8_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                      const float* d_scale, hipStream_t stream) {
   if (d_scale == nullptr) return FP8MOT_ERR_UNSUPPORTED;

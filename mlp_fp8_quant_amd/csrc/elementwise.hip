@@ -151,6 +151,66 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
   }
 }
 
+// Read/write ceiling for the byte mix of the two HBM-bound kernels, with no
+// arithmetic: NIN = 1 reads 2 bytes and writes 1 per element (quantize),
+// NIN = 2 reads 2 + 2 and writes 1 (two-input SwiGLU).  Same loop, unroll,
+// nontemporal 128-bit accesses and grid as quant_static_kernel /
+// silu_mul_kernel; each output byte is the low byte of the XOR of its input
+// words, so every load is used.  A measurement aid: the quantize and SwiGLU
+// kernels are judged against what the memory system delivers for their mix.
+template <int NIN>
+__global__ __launch_bounds__(kThreads) void rw_ceiling_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+    uint8_t* __restrict__ out, int64_t n) {
+  const int64_t units = n >> 4;
+  constexpr int UN = 4;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * UN;
+  const u32x4* av = reinterpret_cast<const u32x4*>(a);
+  const u32x4* bv = reinterpret_cast<const u32x4*>(b);
+  u32x4* ov = reinterpret_cast<u32x4*>(out);
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * UN + threadIdx.x; base < units;
+       base += stride) {
+    u32x4 x[UN][2 * NIN];
+#pragma unroll
+    for (int k = 0; k < UN; ++k) {
+      const int64_t i = base + k * kThreads;
+      if (i < units) {
+        x[k][0] = __builtin_nontemporal_load(av + 2 * i);
+        x[k][1] = __builtin_nontemporal_load(av + 2 * i + 1);
+        if constexpr (NIN == 2) {
+          x[k][2] = __builtin_nontemporal_load(bv + 2 * i);
+          x[k][3] = __builtin_nontemporal_load(bv + 2 * i + 1);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UN; ++k) {
+      const int64_t i = base + k * kThreads;
+      if (i < units) {
+        u32x4 lo = x[k][0], hi = x[k][1];
+        if constexpr (NIN == 2) {
+          lo ^= x[k][2];
+          hi ^= x[k][3];
+        }
+        // byte j of the output: low byte of input word j
+        auto pick = [](uint32_t w0, uint32_t w1) {
+          return (w0 & 0xFFu) | ((w0 >> 8) & 0xFF00u) | ((w1 & 0xFFu) << 16) | ((w1 << 8) & 0xFF000000u);
+        };
+        u32x4 o;
+        o.x = pick(lo.x, lo.y);
+        o.y = pick(lo.z, lo.w);
+        o.z = pick(hi.x, hi.y);
+        o.w = pick(hi.z, hi.w);
+        __builtin_nontemporal_store(o, ov + i);
+      }
+    }
+  }
+  if (blockIdx.x == 0) {
+    const int64_t t = (units << 4) + threadIdx.x;
+    if (t < n) out[t] = (uint8_t)(NIN == 2 ? a[t] ^ b[t] : a[t]);
+  }
+}
+
 // One-input SwiGLU for rows whose width I is not a multiple of 16: one
 // element per thread per step (such rows are not 16-byte aligned).
 __global__ __launch_bounds__(kThreads) void silu_mul_adj_scalar_kernel(
@@ -517,6 +577,17 @@ hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
                            int max_blocks, hipStream_t stream) {
   hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(grid_for(n >> 6, 4 * max_blocks)),
                      dim3(kThreads), 0, stream, g, u, q, n, d_s, alpha, beta, 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_t n,
+                             int max_blocks, hipStream_t stream) {
+  if (b == nullptr)
+    hipLaunchKernelGGL(rw_ceiling_kernel<1>, dim3(grid_for(n >> 6, 4 * max_blocks)),
+                       dim3(kThreads), 0, stream, a, b, out, n);
+  else
+    hipLaunchKernelGGL(rw_ceiling_kernel<2>, dim3(grid_for(n >> 6, 4 * max_blocks)),
+                       dim3(kThreads), 0, stream, a, b, out, n);
   return hipGetLastError();
 }
 

@@ -37,6 +37,12 @@ hipError_t launch_silu_mul_adjacent(const uint16_t* x, uint8_t* q, int64_t rows,
                                     int64_t inter, const float* d_s, float alpha,
                                     float beta, int max_blocks, hipStream_t stream);
 
+// Measurement aid: reads a [n] (and b [n] when not NULL) as 16-bit words and
+// writes out [n] bytes, with the access pattern and grid of the quantize
+// (b NULL) or two-input SwiGLU kernel and no arithmetic.
+hipError_t launch_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_t n,
+                             int max_blocks, hipStream_t stream);
+
 // u == nullptr: amax of the BF16 tensor x; otherwise amax of silu(x) * u.
 hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,
                           fp8mot_observer_state_dev* st, int mode, float c,
@@ -80,7 +86,9 @@ hipError_t launch_requant_onto_max(const uint8_t* q, uint8_t* out, int64_t n,
 
 // Gate and up GEMMs of a gated MLP with the SwiGLU-FP8 epilogue in one launch:
 // qh[M,I] = e4m3(silu(bf16(G)) * bf16(U) / sh) with G = qx.wg^T * (sx*sg),
-// U = qx.wu^T * (sx*su); bitwise equal to two BF16 GEMMs + launch_silu_mul.
+// U = qx.wu^T * (sx*su), each summed along K in one running sum; bitwise
+// equal to two BF16 launch_gemm calls + launch_silu_mul whenever those GEMMs
+// sum along K as well (always when I >= H; see gemm_splits_k).
 hipError_t launch_gemm_swiglu(const uint8_t* qx, const uint8_t* wg, const uint8_t* wu,
                               uint8_t* qh, int64_t M, int64_t I, int64_t H,
                               const float* sx, const float* sg, const float* su,

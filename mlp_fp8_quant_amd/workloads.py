@@ -152,6 +152,14 @@ def calib_call(base_bits, pos, gain) -> np.ndarray:
     return to_bf16_bits(x).reshape(base_bits.shape)
 
 
+def calib_spike_values(base_bits, pos, gain) -> np.ndarray:
+    """The BF16 bits of one call at its spike positions only: what
+    calib_call(base_bits, pos, gain).ravel()[pos] holds (every other entry of
+    the call equals the base)."""
+    x = (base_bits.ravel()[pos].astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return to_bf16_bits(x * gain)
+
+
 def forward_input(tower, site, seed=0) -> np.ndarray:
     """Forward-pass input of one site: one further draw of the calibration
     distribution (base tensor of its own, spikes at a fresh per-call gain)."""

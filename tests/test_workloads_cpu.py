@@ -85,3 +85,22 @@ def test_calibration_spikes(tower):
     untouched = np.ones(base.size, bool)
     untouched[pos] = False
     assert np.array_equal(f0[untouched], f1[untouched])
+
+
+@pytest.mark.parametrize("tower", ["und", "gen"])
+def test_spike_values_and_call_amax_shortcut(tower):
+    # calib_spike_values is the materialized call at the spike positions, and
+    # the call's amax is max(amax(base), max |spike values|) (a gain >= 5
+    # never pulls an entry below its base value): checked against the
+    # oracle's amax of the whole materialized call, first and last call of
+    # every site
+    from oracle import observer as oobs
+    for site in workloads.SITES:
+        base = workloads.calib_base(tower, site)
+        a_base = oobs.call_amax(base)
+        for t in (0, workloads.CALIB_CALLS - 1):
+            pos, gain = workloads.calib_spikes(tower, site, t, base.size)
+            x = workloads.calib_call(base, pos, gain)
+            vals = workloads.calib_spike_values(base, pos, gain)
+            assert np.array_equal(vals, x.ravel()[pos])
+            assert np.float32(max(a_base, oobs.call_amax(vals))) == oobs.call_amax(x)
