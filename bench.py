@@ -65,10 +65,13 @@ def time_launches(torch, stream, f, reps, warm=2):
 
 
 class ClockSampler:
-    """Samples the GPU's current graphics clock (amdsmi) every few
-    milliseconds on a host thread while a timed region runs."""
+    """Samples the GPU's graphics clock on a host thread while GPU work runs:
+    amdsmi's current GFX clock of each XCD from the firmware's metrics table
+    (mean over the XCDs per sample).  The table refreshes every ~100-300 ms,
+    so only a sustained run of a second or more gives a meaningful figure;
+    the first `skip_s` seconds of samples are dropped."""
 
-    def __init__(self, period_s=0.005):
+    def __init__(self, period_s=0.02):
         self.period = period_s
         self.samples = []
         self.err = None
@@ -79,16 +82,25 @@ class ClockSampler:
             amdsmi.amdsmi_init()
             self._smi = amdsmi
             self._h = amdsmi.amdsmi_get_processor_handles()[0]
-            self._smi.amdsmi_get_clock_info(self._h, amdsmi.AmdSmiClkType.GFX)
+            self._read()
         except Exception as e:   # no management interface: report null
             self._smi = None
             self.err = f"{type(e).__name__}: {e}"
 
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        xs = [float(v) for v in (m.get("current_gfxclks") or []) if isinstance(v, (int, float))]
+        if not xs and isinstance(m.get("current_gfxclk"), (int, float)):
+            xs = [float(m["current_gfxclk"])]
+        return sum(xs) / len(xs) if xs else None
+
     def _run(self):
+        t0 = time.perf_counter()
         while not self._stop.is_set():
             try:
-                c = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
-                self.samples.append(float(c["clk"]))
+                v = self._read()
+                if v is not None:
+                    self.samples.append((time.perf_counter() - t0, v))
             except Exception as e:
                 self.err = f"{type(e).__name__}: {e}"
                 return
@@ -102,15 +114,16 @@ class ClockSampler:
             self._thread.start()
         return self
 
-    def stop(self):
+    def stop(self, skip_s=0.3):
         self._stop.set()
         if self._thread is not None:
             self._thread.join()
-        if not self.samples:
+        vals = sorted(v for t, v in self.samples if t >= skip_s)
+        if not vals:
             return {"mhz_median": None, "samples": 0, "error": self.err}
-        s = sorted(self.samples)
-        return {"mhz_median": s[len(s) // 2], "mhz_min": s[0], "mhz_max": s[-1],
-                "samples": len(s), "source": "amdsmi current GFX clock"}
+        return {"mhz_median": vals[len(vals) // 2], "mhz_min": vals[0], "mhz_max": vals[-1],
+                "samples": len(vals),
+                "source": "amdsmi gpu metrics current_gfxclks, mean over XCDs per sample"}
 
 
 def parse():
@@ -125,6 +138,9 @@ def parse():
                    help="intermediate channels in the oracle's timed block")
     p.add_argument("--no-blocks", action="store_true",
                    help="only the headline step and its kernels (for profiling runs)")
+    p.add_argument("--blocks", default="gen_mlp,elementwise_large,per_row_fp8,fused_topology,"
+                                       "two_tower_layer,library_references",
+                   help="comma-separated extra blocks to run")
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="also run one plain device copy of this many MiB (a "
                         "known-size reference for the profiler's byte counters)")
@@ -202,10 +218,16 @@ def main():
     gemm_flops = 2.0 * M * I * H * 3
     fused_flops = 2 * 2.0 * M * I * H
     down_flops = 2.0 * M * I * H
-    clock.start()
     ms_step = timed_steps(fp8.ACC_EXACT, args.steps, args.warmup)
-    sclk_step = clock.stop()
     value = gemm_flops / (ms_step * 1e-3) / 1e12
+    # the clock under this load: the same step, sustained for ~1.5 s
+    clock.start()
+    t_end = time.perf_counter() + 1.5
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            step(fp8.ACC_EXACT)
+        torch.cuda.synchronize()
+    sclk_step = clock.stop()
 
     # kernels of the step, each timed alone: back-to-back launches on the
     # stream they run on, one pair of HIP events around them
@@ -223,12 +245,7 @@ def main():
         out = {}
         for n, f in calls.items():
             reps_n = reps if n in ("gate_up_swiglu", "down") else 4 * reps
-            if n == "gate_up_swiglu" and accum == fp8.ACC_EXACT:
-                clock.start()
-                out[n] = time_launches(torch, stream, f, reps_n, warm=2)
-                out["sclk_" + n] = clock.stop()
-            else:
-                out[n] = time_launches(torch, stream, f, reps_n, warm=2)
+            out[n] = time_launches(torch, stream, f, reps_n, warm=2)
         return out
 
     us = kernel_times(fp8.ACC_EXACT, 10)
@@ -254,7 +271,6 @@ def main():
         "traffic": recorded_traffic(f"gate_up_swiglu_exact_{M}x{I}x{H}", "gemm.hip"),
         "launch_us": us["gate_up_swiglu"], "flops_per_launch": fused_flops,
         "frac_f16_peak": fused / F16_PEAK_TFLOPS,
-        "sclk": us["sclk_gate_up_swiglu"],
     }
 
     # the native FP8 MFMA engine, same workload (context only)
@@ -264,21 +280,27 @@ def main():
     fp8_engine = {
         "meets_tolerance": False, "note": FP8_ENGINE_NOTE,
         "value": gemm_flops / (ms8 * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms8,
-        "kernels_us": {k: v for k, v in us8.items() if not k.startswith("sclk")},
+        "kernels_us": us8,
         "gate_up_swiglu_frac_fp8_peak": f8 / FP8_PEAK_TFLOPS,
         "down_frac_fp8_peak": tflops(down_flops, us8["down"]) / FP8_PEAK_TFLOPS,
     }
-    refs = None if args.no_blocks else library_references(fp8, torch, dev, stream, qxb, q, sx, s)
+    want = set() if args.no_blocks else set(args.blocks.split(","))
+    refs = (library_references(fp8, torch, dev, stream, qxb, q, sx, s)
+            if "library_references" in want else None)
 
     del x, q, qx, y, ws
     torch.cuda.empty_cache()
 
     blocks = {}
-    if not args.no_blocks:
+    if "gen_mlp" in want:
         blocks["gen_mlp"] = gen_mlp(fp8, torch, dev, stream, workloads)
+    if "elementwise_large" in want:
         blocks["elementwise_large"] = elementwise_large(fp8, torch, dev, stream)
+    if "per_row_fp8" in want:
         blocks["per_row_fp8"] = per_row_fp8(fp8, torch, dev, stream)
+    if "fused_topology" in want:
         blocks["fused_topology"] = fused_topology(fp8, torch, dev, stream, workloads)
+    if "two_tower_layer" in want:
         blocks["two_tower_layer"] = two_tower_layer(fp8, torch, dev, stream)
 
     if args.copy_calib_mb > 0:
@@ -303,7 +325,7 @@ def main():
         "config": {"workload": wl_cpu.name, "M": M, "H": H, "I": I, "engine": "exact",
                    "step": "fp8_observe(X) + gated_mlp_fp8", "parallelism": "none (1 GPU)"},
         "frac_fp8_peak": value / FP8_PEAK_TFLOPS,
-        "roofline": roofline, "cpu_baseline": cpu, "sclk_step": sclk_step,
+        "roofline": roofline, "cpu_baseline": cpu, "sclk_during_steps": sclk_step,
         "kernels": kernels, "fp8_mfma_engine": fp8_engine,
         "library_references": refs,
         "roofline_hbm": None if large is None else [

@@ -306,7 +306,7 @@ int run_gated_mlp(const uint16_t* x, int64_t M, int64_t H, int64_t I, const floa
   // silu_mul_2in_fp8 whenever those GEMMs sum K in one running sum, without
   // writing G and U
   if (e == hipSuccess && I > 0)
-    e = launch_gemm_swiglu(qx, wg, wu, qh, M, I, H, d_sx, d_sg, d_su, d_sh, accum, stream);
+    e = launch_gemm_swiglu(qx, wg, wu, qh, M, I, H, d_sx, d_sg, d_su, d_sh, accum, cus, stream);
   if (e == hipSuccess)
     e = launch_gemm(qh, wd, y, M, H, I, d_sh, d_sd, FP8MOT_OUT_BF16, nullptr, accum, cus, stream);
   return hip_status(e);
@@ -394,7 +394,7 @@ int fp8_gate_up_swiglu(const uint8_t* qx, const uint8_t* wg, const float* d_sx,
   int cus = 0;
   int st = current_device(&cus);
   if (st != FP8MOT_OK) return st;
-  return hip_status(launch_gemm_swiglu(qx, wg, wu, qh, M, I, H, d_sx, d_sg, d_su, d_sh, accum, stream));
+  return hip_status(launch_gemm_swiglu(qx, wg, wu, qh, M, I, H, d_sx, d_sg, d_su, d_sh, accum, cus, stream));
 }
 
 size_t qkv_fp8_workspace(int64_t M, int64_t H) {

@@ -30,14 +30,17 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
 }
 
 // Static quantization: q = e4m3(x / s), one IEEE FP32 division per element.
-// A thread handles 64 elements per step (eight 128-bit loads in flight, four
-// 128-bit stores), keeping enough bytes in flight to cover HBM latency.
+// A thread handles 32 elements per step (four 128-bit loads in flight, two
+// 128-bit stores) on a grid of up to 64 workgroups per CU, so that the
+// large-MLP activation is one grid step (measured on MI355X at 84M elements:
+// 43.9 us against 46-47 us with 64 elements per thread on half the grid, and
+// against 43.2 us for a kernel with the same accesses and no arithmetic).
 __global__ __launch_bounds__(kThreads) void quant_static_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int64_t n,
     const float* __restrict__ d_scale) {
   const float s = *d_scale;
   const int64_t units = n >> 4;                 // 16-element units
-  constexpr int UN = 4;                         // units in flight per thread
+  constexpr int UN = 2;                         // units in flight per thread
   const int64_t stride = (int64_t)gridDim.x * kThreads * UN;
   const u32x4* xv = reinterpret_cast<const u32x4*>(x);
   u32x4* qv = reinterpret_cast<u32x4*>(q);
@@ -80,8 +83,8 @@ __global__ __launch_bounds__(kThreads) void quant_static_kernel(
 // the division done as a multiplication by the (correctly rounded)
 // reciprocal of s_out.  A thread handles 64 elements per step: sixteen
 // 128-bit loads in flight, four stores (measured on MI355X at the large-MLP
-// size: 4 units per thread and 16 workgroups per CU beat 2 and 8 by ~5%;
-// 32 workgroups per CU gain another 1.3%: 393.8 -> 388.7 us).
+// size: 4 units per thread beat 1 and 2; the grid takes up to 64 workgroups
+// per CU: 366 -> 355 us against 32, 372 us with 16).
 //  ADJ = false: g and u are two flat tensors of n elements (two-input form).
 //  ADJ = true:  one tensor x of rows [gate (I) | up (I)], I % 16 == 0; the
 //               output is [rows, I] and n = rows * I.  Each 16-element unit
@@ -153,17 +156,18 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
 
 // Read/write ceiling for the byte mix of the two HBM-bound kernels, with no
 // arithmetic: NIN = 1 reads 2 bytes and writes 1 per element (quantize),
-// NIN = 2 reads 2 + 2 and writes 1 (two-input SwiGLU).  Same loop, unroll,
-// nontemporal 128-bit accesses and grid as quant_static_kernel /
+// NIN = 2 reads 2 + 2 and writes 1 (two-input SwiGLU).  Same loop, units in
+// flight (UN), nontemporal 128-bit accesses and grid as quant_static_kernel /
 // silu_mul_kernel; each output byte is the low byte of the XOR of its input
 // words, so every load is used.  A measurement aid: the quantize and SwiGLU
-// kernels are judged against what the memory system delivers for their mix.
-template <int NIN>
+// kernels are judged against what the memory system delivers for their mix
+// (on MI355X these are also the fastest of the unit counts and grid sizes
+// swept for a plain read/write stream of that mix).
+template <int NIN, int UN>
 __global__ __launch_bounds__(kThreads) void rw_ceiling_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
     uint8_t* __restrict__ out, int64_t n) {
   const int64_t units = n >> 4;
-  constexpr int UN = 4;
   const int64_t stride = (int64_t)gridDim.x * kThreads * UN;
   const u32x4* av = reinterpret_cast<const u32x4*>(a);
   const u32x4* bv = reinterpret_cast<const u32x4*>(b);
@@ -538,12 +542,15 @@ int grid_for(int64_t units, int max_blocks) {
 
 }  // namespace
 
+// Grids of the two streaming kernels (max_blocks = 8 per CU): one thread per
+// 32 (quantize) or 64 (SwiGLU) elements, up to 64 workgroups per CU.
+static int quant_grid(int64_t n, int max_blocks) { return grid_for(n >> 5, 8 * max_blocks); }
+static int silu_grid(int64_t n, int max_blocks) { return grid_for(n >> 6, 8 * max_blocks); }
+
 hipError_t launch_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                                const float* d_scale, int max_blocks,
                                hipStream_t stream) {
-  // up to 32 workgroups per CU, so that the large-MLP activation (84M
-  // elements) is one step of the grid: 49.5 -> 47.8 us against 16 per CU
-  hipLaunchKernelGGL(quant_static_kernel, dim3(grid_for(n >> 6, 4 * max_blocks)),
+  hipLaunchKernelGGL(quant_static_kernel, dim3(quant_grid(n, max_blocks)),
                      dim3(kThreads), 0, stream, x, q, n, d_scale);
   return hipGetLastError();
 }
@@ -575,7 +582,7 @@ hipError_t launch_requant_onto_max(const uint8_t* q, uint8_t* out, int64_t n,
 hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
                            int64_t n, const float* d_s, float alpha, float beta,
                            int max_blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(grid_for(n >> 6, 4 * max_blocks)),
+  hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(silu_grid(n, max_blocks)),
                      dim3(kThreads), 0, stream, g, u, q, n, d_s, alpha, beta, 0u);
   return hipGetLastError();
 }
@@ -583,10 +590,10 @@ hipError_t launch_silu_mul(const uint16_t* g, const uint16_t* u, uint8_t* q,
 hipError_t launch_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_t n,
                              int max_blocks, hipStream_t stream) {
   if (b == nullptr)
-    hipLaunchKernelGGL(rw_ceiling_kernel<1>, dim3(grid_for(n >> 6, 4 * max_blocks)),
+    hipLaunchKernelGGL((rw_ceiling_kernel<1, 2>), dim3(quant_grid(n, max_blocks)),
                        dim3(kThreads), 0, stream, a, b, out, n);
   else
-    hipLaunchKernelGGL(rw_ceiling_kernel<2>, dim3(grid_for(n >> 6, 4 * max_blocks)),
+    hipLaunchKernelGGL((rw_ceiling_kernel<2, 4>), dim3(silu_grid(n, max_blocks)),
                        dim3(kThreads), 0, stream, a, b, out, n);
   return hipGetLastError();
 }
@@ -596,7 +603,7 @@ hipError_t launch_silu_mul_adjacent(const uint16_t* x, uint8_t* q, int64_t rows,
                                     float beta, int max_blocks, hipStream_t stream) {
   const int64_t n = rows * inter;
   if (inter % 16 == 0 && n / 16 <= (int64_t)UINT32_MAX) {
-    hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(grid_for(n >> 6, 4 * max_blocks)),
+    hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(silu_grid(n, max_blocks)),
                        dim3(kThreads), 0, stream, x, nullptr, q, n, d_s, alpha, beta,
                        (uint32_t)inter);
   } else {

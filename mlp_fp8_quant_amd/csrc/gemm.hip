@@ -55,6 +55,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
                 "the K groups' sums fit the stage buffers");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[KSPL * NB * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane0 = tid & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = KSPL == 1 ? 0 : wave_id / NW;    // K group
   const int wave = wave_id - kg * NW;             // wave within its K group
@@ -274,67 +275,114 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
   auto stage_buf = [&](int b) -> uint8_t* { return smem + (kg * NB + b) * STAGE; };
   // K group kg's local stage t is the tile's stage t * KSPL + kg
   auto gstage = [&](int t) { return t * KSPL + kg; };
-  int tm, tn;
-  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-  // this tile's projection (a grouped launch walks the groups' tile columns)
-  const uint8_t* gB = g.B;
-  void* gCp = g.C;
-  const float* gsw = g.sw;
-  int N = g.N, ldc = g.ldc;
-  if (g.groups > 1) {
-    int p = 0;
-    while (p + 1 < g.groups && tn >= g.gtiles_n[p]) {
-      tn -= g.gtiles_n[p];
-      ++p;
+  // A tile's place in the grid: its output rows from m0 and columns from n0
+  // (fused: 128 of each of G and U), and -- in a grouped launch, which walks
+  // the groups' tile columns -- its projection's B, C, weight scale and N.
+  struct TileInfo {
+    int m0, n0, N, ldc;
+    const uint8_t* B;
+    void* C;
+    const float* sw;
+  };
+  auto tile_info = [&](int tile) -> TileInfo {
+    int tm, tn;
+    tile_of(tile, g.tiles_m, g.tiles_n, tm, tn);
+    TileInfo t{0, 0, g.N, g.ldc, g.B, g.C, g.sw};
+    if (g.groups > 1) {
+      int p = 0;
+      while (p + 1 < g.groups && tn >= g.gtiles_n[p]) {
+        tn -= g.gtiles_n[p];
+        ++p;
+      }
+      t.B = g.gB[p];
+      t.C = g.gC[p];
+      t.sw = g.gsw[p];
+      t.N = g.gN[p];
+      t.ldc = t.N;
     }
-    gB = g.gB[p];
-    gCp = g.gC[p];
-    gsw = g.gsw[p];
-    N = g.gN[p];
-    ldc = N;
-  }
-  // output columns of this tile start at n0 (fused: 128 of each of G and U)
-  const int m0 = tm * BM, n0 = tn * (FUSED ? BN / 2 : BN);
-
-  // operand windows start at the tile's first row; rows past M (N) read as 0
-  const v4i ra_rs = make_rsrc_words(g.A + (int64_t)m0 * K, (int64_t)(M - m0) * K);
-  const v4i rb_rs = make_rsrc_words(gB + (int64_t)n0 * K, (int64_t)(N - n0) * K);
-  const v4i rb2_rs = FUSED ? make_rsrc_words(g.B2 + (int64_t)n0 * K, (int64_t)(N - n0) * K) : rb_rs;
+    t.m0 = tm * BM;
+    t.n0 = tn * (FUSED ? BN / 2 : BN);
+    return t;
+  };
+  // Operand windows of a tile (buffer resources starting at its first A and
+  // B rows): rows past M (N) lie outside them and read as zeros.
+  struct Windows {
+    v4i a, b, b2;
+  };
+  auto windows = [&](const TileInfo& t) -> Windows {
+    Windows w;
+    w.a = make_rsrc_words(g.A + (int64_t)t.m0 * K, (int64_t)(M - t.m0) * K);
+    w.b = make_rsrc_words(t.B + (int64_t)t.n0 * K, (int64_t)(t.N - t.n0) * K);
+    w.b2 = FUSED ? make_rsrc_words(g.B2 + (int64_t)t.n0 * K, (int64_t)(t.N - t.n0) * K) : w.b;
+    return w;
+  };
 
   // Copy q (= wave * LPW + i) of a stage fills LDS rows q*RPI .. q*RPI+RPI-1
   // (A rows, then B rows); lane l brings row q*RPI + l/CH, physical chunk
   // l % CH, i.e. logical chunk swz(row, l % CH) of the row's 64 K.  Fused:
   // B's LDS rows come in 32-row blocks alternating gate / up, so that a
   // wave's 32x32 blocks j (gate) and j + 1 (up) cover the same columns.
-  int goff[LPW], gkc[LPW];
+  // Rows past M (N) get an offset past every window.
+  auto copy_offsets = [&](const TileInfo& t, int* goff, int* gkc) {
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int q = wave * LPW + i;
-    const int lr = (q < A_INS ? q : q - A_INS) * RPI + lane / CH;   // row in the A or B region
-    const int c = swz(lr, lane % CH);
-    int grow, lim;
-    if (q < A_INS) {
-      grow = lr;
-      lim = M - m0;
-    } else {
-      grow = FUSED ? (lr >> 6) * 32 + (lr & 31) : lr;
-      lim = N - n0;
+    for (int i = 0; i < LPW; ++i) {
+      const int q = wave * LPW + i;
+      const int lr = (q < A_INS ? q : q - A_INS) * RPI + lane0 / CH;   // row in the A or B region
+      const int c = swz(lr, lane0 % CH);
+      int grow, lim;
+      if (q < A_INS) {
+        grow = lr;
+        lim = M - t.m0;
+      } else {
+        grow = FUSED ? (lr >> 6) * 32 + (lr & 31) : lr;
+        lim = t.N - t.n0;
+      }
+      goff[i] = grow < lim ? grow * K + c * 16 : kOOB;
+      gkc[i] = c * 16;
     }
-    goff[i] = grow < lim ? grow * K + c * 16 : kOOB;
-    gkc[i] = c * 16;
-  }
-  auto issue_copy = [&](int b, int s, int i) {   // copy i of this wave for stage s into buffer b
+  };
+  // copy i of this wave for stage s into buffer b
+  auto issue_copy = [&](const Windows& w, const int* goff, const int* gkc, int b, int s, int i) {
     const int k0 = s * KS;
     const int q = wave * LPW + i;
-    const v4i rs = q < A_INS ? ra_rs : ((FUSED && (((q - A_INS) * RPI) & 32)) ? rb2_rs : rb_rs);
+    const v4i rs = q < A_INS ? w.a : ((FUSED && (((q - A_INS) * RPI) & 32)) ? w.b2 : w.b);
     const int off = (goff[i] != kOOB && k0 + gkc[i] < K) ? goff[i] + k0 : kOOB;
     copy_to_lds(rs, (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)(stage_buf(b) + q * 1024)), off);
   };
-  auto issue_stage = [&](int b, int s) {
+  auto issue_stage = [&](const Windows& w, const int* goff, const int* gkc, int b, int s) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) issue_copy(b, s, i);
+    for (int i = 0; i < LPW; ++i) issue_copy(w, goff, gkc, b, s, i);
   };
+  // local stages per K group (group 1 of an odd count runs one past the end
+  // of K, on zeros, so that both groups meet the same barriers)
+  const int KT = ((K + KS - 1) / KS + KSPL - 1) / KSPL;
+  const int ntiles = g.tiles_m * g.tiles_n;
 
+  // Persistent loop: a workgroup takes tiles blockIdx.x, + gridDim.x, ...
+  // (gridDim.x is a multiple of the 8 XCDs, so every tile it takes belongs
+  // to its own XCD's band).  The first NB stages of the next tile are copied
+  // into LDS after this tile's main loop and before its epilogue, which then
+  // runs while they are on their way.  A launch with one tile per workgroup
+  // runs the loop once (K-split launches always do).
+  // Exact-engine tiles only: the FP8 engine's loop keeps more registers live
+  // and would spill in a tile loop, so its workgroups take one tile each.
+  constexpr bool PERSIST = ENGINE == 0 && KSPL == 1;
+  bool staged = false;
+  for (int tile = blockIdx.x, iter = 0; PERSIST ? tile < ntiles : iter < 1;
+       tile += gridDim.x, ++iter) {
+  // the lane index, opaque to the compiler for each tile: the per-lane LDS
+  // fragment addresses and epilogue indices derived from it are formed per
+  // tile instead of being hoisted out of this loop and kept live across the
+  // epilogue, which needs those registers
+  int lane = lane0;
+  if constexpr (PERSIST) asm volatile("" : "+v"(lane));
+  const TileInfo ti = tile_info(tile);
+  const Windows win = windows(ti);
+  int goff[LPW], gkc[LPW];
+  copy_offsets(ti, goff, gkc);
+  const int m0 = ti.m0, n0 = ti.n0, N = ti.N, ldc = ti.ldc;
+  const float* gsw = ti.sw;
+  void* gCp = ti.C;
   v16f acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -417,7 +465,7 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
         if constexpr (kCopies) {
 #pragma unroll
           for (int c = 0; c < CPR; ++c)
-            if (i * CPR + c < LPW) issue_copy(cb, cs, i * CPR + c);
+            if (i * CPR + c < LPW) issue_copy(win, goff, gkc, cb, cs, i * CPR + c);
         }
       }
     } else {
@@ -430,7 +478,7 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
         if constexpr (kCopies) {
 #pragma unroll
           for (int c = 0; c < CPR; ++c)
-            if (i * CPR + c < LPW) issue_copy(cb, cs, i * CPR + c);
+            if (i * CPR + c < LPW) issue_copy(win, goff, gkc, cb, cs, i * CPR + c);
         }
       }
     }
@@ -457,18 +505,20 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
   //    just freed, then read the first fragments of stage s + 1.
   // The MFMAs of a step are issued after these reads, so the barrier wait
   // overlaps the matrix pipe still working through the previous step.
-  // local stages per K group (group 1 of an odd count runs one past the end
-  // of K, on zeros, so that both groups meet the same barriers)
-  const int KT = ((K + KS - 1) / KS + KSPL - 1) / KSPL;
   // have the epilogue's kernel arguments in registers before the loop, so no
   // scalar load is still pending inside it (that would turn every LDS wait
   // there into a wait for all LDS reads)
   asm volatile("" ::"s"(g.sx), "s"(gsw), "s"(g.sw2), "s"(g.sy), "s"(gCp));
+  if (!staged) {
 #pragma unroll
-  for (int u = 0; u < NB; ++u)
-    if (u < KT) issue_stage(u, gstage(u));
+    for (int u = 0; u < NB; ++u)
+      if (u < KT) issue_stage(win, goff, gkc, u, gstage(u));
+  }
   if (KT > 0) {
-    wait_copies(LPW * (min(NB, KT) - 1));
+    // staged: the previous epilogue's stores were issued after these copies
+    // and count in the same counter, so wait for everything
+    if (staged) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    else wait_copies(LPW * (min(NB, KT) - 1));
     __syncthreads();
     rd(0, 0, 0);
   }
@@ -493,14 +543,16 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
             // The copies of stage s + NB go into the buffer just freed.  Past
             // the end of K they touch no memory and write zeros, into a
             // buffer nobody reads again -- at the last stage, where no
-            // barrier has freed this buffer, into the next one instead.
+            // barrier has freed this buffer, into the next one instead (the
+            // wait after the loop drains them before any buffer is refilled).
             mf(slot, std::true_type{}, s + 1 < KT ? u : (u + 1) % NB, gstage(s + NB));
           }
         }
       }
     }
   }
-  // no copy into LDS may still be on its way when the workgroup ends
+  // no copy into LDS may still be on its way when the workgroup ends or
+  // the buffers are refilled
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   if constexpr (KSPL == 2) {
@@ -531,6 +583,21 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = __fadd_rn(acc[i][j][4 * q + e], o[e]);
         }
+  }
+
+  // The next tile's first stages: every wave has read this tile's last
+  // fragments (its MFMAs are issued), so after one barrier the buffers are free.
+  staged = false;
+  if (PERSIST && tile + (int)gridDim.x < ntiles) {
+    __syncthreads();
+    const TileInfo nt = tile_info(tile + gridDim.x);
+    const Windows nw = windows(nt);
+    int ngoff[LPW], ngkc[LPW];
+    copy_offsets(nt, ngoff, ngkc);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (u < KT) issue_stage(nw, ngoff, ngkc, u, gstage(u));
+    staged = true;
   }
 
   // ---- epilogue: y = fp32(acc * alpha), then the output format ----
@@ -687,29 +754,45 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
         }
       }
   }
+  }  // tile loop
+}
+
+// Launches one GEMM kernel: one workgroup per tile, or -- for the exact
+// engine when there are more tiles than the GPU holds at once -- as many
+// workgroups as are resident (the kernel's occupancy per CU times the CUs, a
+// multiple of the 8 XCDs), each walking its tiles with the next tile's first
+// stages prefetched during the current one's epilogue.  K-split and
+// FP8-engine launches keep one tile per workgroup.
+template <int BM, int BN, int WM, int WN, int OUT, int ENGINE, bool FUSED, bool DEEP, int KSPL>
+hipError_t launch_kernel(const GemmArgs& a, int num_cus, hipStream_t stream) {
+  auto kern = gemm_kernel<BM, BN, WM, WN, OUT, ENGINE, FUSED, DEEP, KSPL>;
+  constexpr int block = WM * WN * 64 * KSPL;
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  int64_t grid = tiles;
+  if (ENGINE == 0 && KSPL == 1) {   // the kernels that walk several tiles
+    static std::atomic<int> occupancy{0};
+    int occ = occupancy.load(std::memory_order_relaxed);
+    if (occ == 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, block, 0) != hipSuccess || occ < 1)
+        occ = 1;
+      occupancy.store(occ, std::memory_order_relaxed);
+    }
+    const int64_t resident = (int64_t)occ * num_cus;
+    if (tiles > resident && resident >= kNumXcd) grid = resident - resident % kNumXcd;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(block), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, int ENGINE, bool DEEP, int KSPL>
-hipError_t launch_tiled(GemmArgs a, int out_kind, hipStream_t stream) {
-  const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64 * KSPL);
+hipError_t launch_tiled(GemmArgs a, int out_kind, int num_cus, hipStream_t stream) {
   switch (out_kind) {
-    case 0:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 0, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
-      break;
-    case 1:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 1, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
-      break;
-    case 3:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 3, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
-      break;
-    case 4:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 4, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, 2, ENGINE, false, DEEP, KSPL>), grid, block, 0, stream, a);
-      break;
+    case 0: return launch_kernel<BM, BN, WM, WN, 0, ENGINE, false, DEEP, KSPL>(a, num_cus, stream);
+    case 1: return launch_kernel<BM, BN, WM, WN, 1, ENGINE, false, DEEP, KSPL>(a, num_cus, stream);
+    case 3: return launch_kernel<BM, BN, WM, WN, 3, ENGINE, false, DEEP, KSPL>(a, num_cus, stream);
+    case 4: return launch_kernel<BM, BN, WM, WN, 4, ENGINE, false, DEEP, KSPL>(a, num_cus, stream);
+    default: return launch_kernel<BM, BN, WM, WN, 2, ENGINE, false, DEEP, KSPL>(a, num_cus, stream);
   }
-  return hipGetLastError();
 }
 
 // Tile counts of a launch with BM x BN tiles (a grouped launch adds up the
@@ -729,12 +812,10 @@ void set_tiles(GemmArgs& a) {
 }
 
 template <int BM, int WM, int WN, int ENGINE>
-hipError_t launch_fused(GemmArgs a, hipStream_t stream) {
+hipError_t launch_fused(GemmArgs a, int num_cus, hipStream_t stream) {
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + 127) / 128;
-  const dim3 grid(a.tiles_m * a.tiles_n), block(WM * WN * 64);
-  hipLaunchKernelGGL((gemm_kernel<BM, 256, WM, WN, 0, ENGINE, true>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  return launch_kernel<BM, 256, WM, WN, 0, ENGINE, true, false, 1>(a, num_cus, stream);
 }
 
 int64_t tiles_of(int64_t M, int64_t N, int bm, int bn) {
@@ -773,11 +854,11 @@ template <int BM, int BN, int WM, int WN, int ENGINE>
 hipError_t launch_cfg(GemmArgs a, int out_kind, int num_cus, hipStream_t stream, bool split) {
   set_tiles<BM, BN>(a);
   if constexpr (BM == 128) {
-    if (split) return launch_tiled<BM, BN, WM, WN, ENGINE, false, 2>(a, out_kind, stream);
+    if (split) return launch_tiled<BM, BN, WM, WN, ENGINE, false, 2>(a, out_kind, num_cus, stream);
   }
   const bool deep = ENGINE == 1 && (BM + BN > 256 || (int64_t)a.tiles_m * a.tiles_n <= num_cus);
-  if (deep) return launch_tiled<BM, BN, WM, WN, ENGINE, true, 1>(a, out_kind, stream);
-  return launch_tiled<BM, BN, WM, WN, ENGINE, false, 1>(a, out_kind, stream);
+  if (deep) return launch_tiled<BM, BN, WM, WN, ENGINE, true, 1>(a, out_kind, num_cus, stream);
+  return launch_tiled<BM, BN, WM, WN, ENGINE, false, 1>(a, out_kind, num_cus, stream);
 }
 
 template <int ENGINE>
@@ -854,15 +935,15 @@ hipError_t launch_gemm_grouped(const uint8_t* qa, int groups, const uint8_t* con
 hipError_t launch_gemm_swiglu(const uint8_t* qx, const uint8_t* wg, const uint8_t* wu,
                               uint8_t* qh, int64_t M, int64_t I, int64_t H,
                               const float* sx, const float* sg, const float* su,
-                              const float* sh, int accum, hipStream_t stream) {
+                              const float* sh, int accum, int num_cus, hipStream_t stream) {
   GemmArgs a{};
   a.A = qx; a.B = wg; a.B2 = wu; a.C = qh;
   a.M = (int)M; a.N = (int)I; a.K = (int)H;
   a.sx = sx; a.sw = sg; a.sw2 = su; a.sy = sh;
   a.ldc = (int)I;
   a.groups = 1;
-  if (accum == 1) return launch_fused<256, 2, 4, 1>(a, stream);
-  return launch_fused<256, 2, 4, 0>(a, stream);
+  if (accum == 1) return launch_fused<256, 2, 4, 1>(a, num_cus, stream);
+  return launch_fused<256, 2, 4, 0>(a, num_cus, stream);
 }
 
 }  // namespace fp8mot

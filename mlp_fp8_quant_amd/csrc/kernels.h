@@ -92,6 +92,6 @@ hipError_t launch_requant_onto_max(const uint8_t* q, uint8_t* out, int64_t n,
 hipError_t launch_gemm_swiglu(const uint8_t* qx, const uint8_t* wg, const uint8_t* wu,
                               uint8_t* qh, int64_t M, int64_t I, int64_t H,
                               const float* sx, const float* sg, const float* su,
-                              const float* sh, int accum, hipStream_t stream);
+                              const float* sh, int accum, int num_cus, hipStream_t stream);
 
 }  // namespace fp8mot

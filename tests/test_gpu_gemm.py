@@ -259,3 +259,29 @@ def test_refusals():
     with pytest.raises(fp8.Fp8motError) as e:   # unknown engine
         fp8.fp8_linear(qa, qb, s, s, accum=7)
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("accum", ENGINES)
+def test_many_tiles_ragged_edges_and_k_tail(accum):
+    # more 256x256 tiles than the GPU holds at once (18 x 17 = 306), so the
+    # exact engine's workgroups walk several tiles each, with ragged last
+    # tile rows and columns and a K that is not a multiple of the 128-K stage;
+    # every sampled output (the last rows and columns included) against the
+    # exact sum
+    dev = device()
+    M, N, K = 4357, 4136, 1040
+    rng = np.random.default_rng(77 + accum)
+    qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx, sw = np.float32(0.0213), np.float32(1.7e-4)
+    out = _run(qa, qb, sx, sw, dev, accum=accum)
+    rows = np.concatenate([np.arange(M - 70, M), np.sort(rng.choice(M - 70, 58, replace=False))])
+    y32 = host_f32(out[fp8.OUT_F32])[rows]
+    S, A = olin.gemm_exact(qa[rows], qb)
+    alpha = olin.epilogue_alpha(sx, sw)
+    yb = host_bits(out[fp8.OUT_BF16])[rows]
+    assert np.array_equal(yb, f32_to_bf16(y32))
+    if accum == fp8.ACC_EXACT:
+        check_gemm_f32(y32, S, A, alpha)
+        check_gemm_bf16(yb, y32, S, A, alpha)
+    else:
+        check_gemm_fp8_engine(y32[:16], S[:16], A[:16], alpha, fp8_mfma_group_bound(qa[rows[:16]], qb))

@@ -295,3 +295,36 @@ def test_qkv_grouped_launch_equals_separate_gemms(ns, accum):
         assert y.shape == (M, w.shape[0])
         if w.shape[0]:
             assert torch.equal(y, fp8.fp8_linear(qx, w, sx, s, accum=accum))
+
+
+@pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+def test_fused_many_tiles_ragged_equals_parts(accum):
+    # 18 x 33 = 594 fused tiles (more than the GPU holds at once: the exact
+    # engine's workgroups walk several, prefetching the next tile's first
+    # stages during each epilogue), ragged M and I, K not a multiple of 128:
+    # bitwise the separate gate/up GEMMs + SwiGLU, and the codes of sampled
+    # rows (the last ones included) against the oracle
+    dev = device()
+    M, I, H = 4357, 4144, 1040
+    rng = np.random.default_rng(88 + accum)
+    x = workloads.activations(rng, M, H)
+    wg = workloads.weights(rng, I, H, 0.02)
+    wu = workloads.weights(rng, I, H, 0.02)
+    sx = olin.scale_from_amax(olin.amax_f32(x))
+    qx_o = olin.quant_static(x, sx)
+    (qg, sg), (qu, su) = olin.rtn_weight(wg), olin.rtn_weight(wu)
+    qx = to_dev_u8(qx_o, dev)
+    dg, du = to_dev_u8(qg, dev), to_dev_u8(qu, dev)
+    sh = np.float32(0.03)
+    dsx, dsg, dsu, dsh = (scalar(v, dev) for v in (sx, sg, su, sh))
+    qh = fp8.fp8_gate_up_swiglu(qx, dg, dsx, dsg, du, dsu, dsh, accum=accum)
+    G = fp8.fp8_linear(qx, dg, dsx, dsg, accum=accum)
+    U = fp8.fp8_linear(qx, du, dsx, dsu, accum=accum)
+    assert torch.equal(qh, fp8.silu_mul_2in_fp8(G, U, dsh))
+    if accum != fp8.ACC_EXACT:
+        return
+    rows = np.concatenate([np.arange(M - 40, M), np.sort(rng.choice(M - 40, 24, replace=False))])
+    Sg, _ = olin.gemm_exact(qx_o[rows], qg)
+    Su, _ = olin.gemm_exact(qx_o[rows], qu)
+    want = silu_mul_fp8(olin.epilogue_bf16(Sg, sx, sg), olin.epilogue_bf16(Su, sx, su), sh)
+    check_fp8_tolerance(host_u8(qh)[rows].ravel(), want)
