@@ -70,6 +70,34 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
   return w ^ nan_bytes;
 }
 
+// x / s for the E4M3 encoder, bit for bit the IEEE quotient where it matters,
+// in four operations instead of a full division (whose ~11 instructions per
+// element made the quantize kernel partly VALU-bound).  Valid for a scale s
+// in [2^-60, 2^60] with r = 1 / s (correctly rounded) and lim = 1024 * s:
+//  * x is first clamped to +-lim (NaN-propagating): |x / s| > 1024 encodes
+//    to +-448 either way, and the clamp keeps the steps below finite;
+//  * q0 = x * r is within one ulp of x / s, the remainder e = x - q0 * s is
+//    exact with an FMA, and q0 + e * r rounded once is the correctly rounded
+//    quotient (Markstein's theorem: r correctly rounded, q0 within one ulp,
+//    no step overflows or underflows -- which holds for |x / s| in
+//    [2^-71, 1024] given the range of s);
+//  * below that, the quotient underflows, the result stays far below the
+//    smallest E4M3 subnormal and encodes to zero;
+//  * the sign of x is put back (a -0 input would otherwise come out +0).
+// Checked against the IEEE division for every BF16 input at 30,000 scales
+// (host FMA), and on the GPU against the oracle by the exhaustive quantize
+// tests.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r, float lim) {
+  const float xc = __builtin_elementwise_minimum(__builtin_elementwise_maximum(x, -lim), lim);
+  const float q0 = __fmul_rn(xc, r);
+  const float e = __builtin_fmaf(-q0, s, xc);
+  const float q1 = __builtin_fmaf(e, r, q0);
+  return __builtin_copysignf(q1, xc);
+}
+__device__ __forceinline__ bool div_by_scale_ok(float s) {
+  return s >= 0x1p-60f && s <= 0x1p60f;
+}
+
 // SiLU(g) * u in FP32: g * (1 / (1 + exp(-g))) * u, with the hardware
 // exponential and reciprocal (about 1 ulp each).  For very negative g,
 // exp(-g) overflows to +Inf, its reciprocal is 0 and the result is a zero

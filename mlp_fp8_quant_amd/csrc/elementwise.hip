@@ -29,7 +29,8 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float* f) {
   }
 }
 
-// Static quantization: q = e4m3(x / s), one IEEE FP32 division per element.
+// Static quantization: q = e4m3(x / s) with the IEEE FP32 quotient's codes
+// (div_by_scale for scales in [2^-60, 2^60], the division itself otherwise).
 // A thread handles 32 elements per step (four 128-bit loads in flight, two
 // 128-bit stores) on a grid of up to 64 workgroups per CU, so that the
 // large-MLP activation is one grid step (measured on MI355X at 84M elements:
@@ -39,6 +40,8 @@ __global__ __launch_bounds__(kThreads) void quant_static_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ q, int64_t n,
     const float* __restrict__ d_scale) {
   const float s = *d_scale;
+  const bool fast = div_by_scale_ok(s);         // uniform
+  const float r = 1.0f / s, lim = 1024.0f * s;
   const int64_t units = n >> 4;                 // 16-element units
   constexpr int UN = 2;                         // units in flight per thread
   const int64_t stride = (int64_t)gridDim.x * kThreads * UN;
@@ -62,8 +65,13 @@ __global__ __launch_bounds__(kThreads) void quant_static_kernel(
         float f[16];
         unpack8(a[k][0], f);
         unpack8(a[k][1], f + 8);
+        if (fast) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) f[j] = f[j] / s;   // IEEE division
+          for (int j = 0; j < 16; ++j) f[j] = div_by_scale(f[j], s, r, lim);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) f[j] = f[j] / s;   // IEEE division
+        }
         u32x4 o;
         o.x = e4m3_pack4(f[0], f[1], f[2], f[3]);
         o.y = e4m3_pack4(f[4], f[5], f[6], f[7]);
@@ -235,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void silu_mul_adj_scalar_kernel(
 // per-channel weights, per-token activations).  One workgroup per row of K
 // elements (K % 16 == 0).  The row's amax is the integer max of
 // (bits & 0x7FFF) -- exact, and NaN patterns sort above Inf; scale =
-// fp32(amax) / 448; q = e4m3(x / s) with one IEEE division per element.  A
+// fp32(amax) / 448; q = e4m3(x / s) with the IEEE quotient's codes
+// (div_by_scale when the row's scale is in its range).  A
 // zero row (s = 0) keeps its signed zeros; a NaN row gets a NaN scale and
 // all-NaN codes.  UH > 0: the row stays in registers between the amax and
 // the quantization (up to UH 16-element units per thread); UH == 0: the row
@@ -260,7 +269,11 @@ __global__ __launch_bounds__(kThreads) void quant_per_row_kernel(
     float f[16];
     unpack8(a, f);
     unpack8(b, f + 8);
-    if (s != 0.0f) {
+    if (div_by_scale_ok(s)) {                          // uniform per row
+      const float r = 1.0f / s, lim = 1024.0f * s;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) f[j] = div_by_scale(f[j], s, r, lim);
+    } else if (s != 0.0f) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) f[j] = f[j] / s;   // IEEE division
     }
