@@ -132,7 +132,7 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=8192,
+    p.add_argument("--cpu-rows", type=int, default=16384,
                    help="rows of X in the oracle's timed block")
     p.add_argument("--cpu-channels", type=int, default=5120,
                    help="intermediate channels in the oracle's timed block")
