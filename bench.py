@@ -20,7 +20,9 @@ Printed: one JSON line.  ``value`` is gated-MLP TFLOP/s (3 GEMMs, 2*M*N*K
 each, over the step time).  ``roofline`` is for the dominant kernel (the
 fused gate/up GEMMs with the SwiGLU-FP8 epilogue) against the FP8 dense MFMA
 peak the metric names, with its average launch time measured with HIP events
-on the stream it runs on.  ``cpu_baseline`` times the CPU oracle on a bounded
+on the stream it runs on, and beside the rate the matrix cores sustain on the
+step's own operand codes with nothing else in the loop (``mfma_ceiling``).
+``cpu_baseline`` times the CPU oracle on a bounded
 block of the same workload.  Further blocks: the native FP8 MFMA engine
 (flagged: below the path's tolerance), vendor-library GEMMs at the same
 shape, the gen-tower gated MLP, the HBM-bound kernels beside a read/write
@@ -62,6 +64,37 @@ def time_launches(torch, stream, f, reps, warm=2):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps * 1e3
+
+
+def mfma_ceiling_against(fp8, torch, stream, kernel, flops, a, b, accum, rounds=3,
+                         window_s=0.3):
+    """A GEMM kernel beside the MFMA ceiling on the same operand codes: the
+    library's dense MFMA loop (fp8mot_mfma_ceiling; fragments taken from the
+    codes in a and b, nothing else in the loop) sized to last about as long
+    as one kernel launch, the two timed alternately `rounds` times in
+    windows of ~window_s each (so both run in the same power and clock
+    state); medians.  kernel(r) launches the GEMM, which does `flops`."""
+    sink = torch.zeros(1, dtype=torch.float32, device=a.device)
+    probe_iters = 1000
+    t_probe = time_launches(torch, stream,
+                            lambda r: fp8.mfma_ceiling(a, b, probe_iters, sink, accum), 3, warm=1)
+    t_kernel = time_launches(torch, stream, kernel, 2, warm=1)
+    iters = max(probe_iters, int(probe_iters * t_kernel / t_probe))
+    per_launch = fp8.mfma_ceiling(a, b, iters, sink, accum)
+    reps = max(3, int(window_s * 1e6 / t_kernel))
+    ks, cs = [], []
+    for _ in range(rounds):
+        ks.append(time_launches(torch, stream, kernel, reps, warm=1))
+        cs.append(time_launches(torch, stream,
+                                lambda r: fp8.mfma_ceiling(a, b, iters, sink, accum), reps, warm=1))
+    k, c = sorted(ks)[rounds // 2], sorted(cs)[rounds // 2]
+    torch.cuda.synchronize()
+    assert float(sink.item()) == 0.0
+    ceiling = per_launch / c / 1e6
+    achieved = flops / k / 1e6
+    return {"ceiling_TFLOP/s": ceiling, "ceiling_launch_us": c, "ceiling_iters": iters,
+            "kernel_TFLOP/s_same_windows": achieved, "kernel_launch_us_same_windows": k,
+            "frac_of_ceiling": achieved / ceiling}
 
 
 class ClockSampler:
@@ -272,6 +305,15 @@ def main():
         "launch_us": us["gate_up_swiglu"], "flops_per_launch": fused_flops,
         "frac_f16_peak": fused / F16_PEAK_TFLOPS,
     }
+    # the same kernel beside what the F16 matrix cores sustain on the step's own
+    # operand codes with nothing else in the loop
+    fused_call = lambda r: fp8.fp8_gate_up_swiglu(qxb, q["gate"], sx, s["gate"], q["up"], s["up"],
+                                                  sh, out=qh, accum=fp8.ACC_EXACT)
+    roofline["mfma_ceiling"] = {
+        "kind": "dense v_mfma_f32_32x32x16_f16 loop on fragments of the step's own X and W_gate "
+                "codes (fp8mot_mfma_ceiling), timed alternately with the kernel",
+        **mfma_ceiling_against(fp8, torch, stream, fused_call, fused_flops, qxb, q["gate"],
+                               fp8.ACC_EXACT)}
 
     # the native FP8 MFMA engine, same workload (context only)
     ms8 = timed_steps(fp8.ACC_FP8_MFMA, max(args.steps // 2, 5), 3)
@@ -284,6 +326,13 @@ def main():
         "gate_up_swiglu_frac_fp8_peak": f8 / FP8_PEAK_TFLOPS,
         "down_frac_fp8_peak": tflops(down_flops, us8["down"]) / FP8_PEAK_TFLOPS,
     }
+    fused8_call = lambda r: fp8.fp8_gate_up_swiglu(qxb, q["gate"], sx, s["gate"], q["up"], s["up"],
+                                                   sh, out=qh, accum=fp8.ACC_FP8_MFMA)
+    fp8_engine["mfma_ceiling"] = {
+        "kind": "dense native FP8 v_mfma_scale_f32_32x32x64_f8f6f4 loop on fragments of the "
+                "same codes, timed alternately with the FP8-engine fused kernel",
+        **mfma_ceiling_against(fp8, torch, stream, fused8_call, fused_flops, qxb, q["gate"],
+                               fp8.ACC_FP8_MFMA)}
     want = set() if args.no_blocks else set(args.blocks.split(","))
     refs = (library_references(fp8, torch, dev, stream, qxb, q, sx, s)
             if "library_references" in want else None)

@@ -150,6 +150,26 @@ uint64_t fp8mot_debug_quant_launches(void);
 int fp8mot_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_t n,
                       hipStream_t stream);
 
+/* Measurement aid, not a step of the path: the rate the matrix cores sustain
+ * on given FP8 data with nothing else in the loop (no copies, LDS, decodes or
+ * epilogue).  MI355X's clock, and with it the MFMA rate, falls under its
+ * power limit by an amount that depends on how much the operand bits toggle,
+ * so the GEMM kernels are judged against this rather than the published
+ * dense peaks alone.  Every wave takes four A fragments from a[0..na) and
+ * four B fragments from b[0..nb) (E4M3 codes, each lane its own, indices
+ * wrapped), then issues 8 * iters MFMAs on four accumulators:
+ * accum = FP8MOT_ACC_EXACT: v_mfma_f32_32x32x16_f16 on the codes decoded
+ * exactly to F16 (2*32*32*16 FLOP each); FP8MOT_ACC_FP8_MFMA: the native
+ * v_mfma_scale_f32_32x32x64_f8f6f4 (2*32*32*64 FLOP each).  Grid: one
+ * 512-thread workgroup per CU.  sink: one device float, written only if the
+ * products sum to a sentinel that finite data never reaches.  *flops (host)
+ * receives the launch's FLOP count.  Refusals: a NULL pointer, na or nb < 64,
+ * iters < 1 or another accum -> FP8MOT_ERR_INVALID_ARG, before any device
+ * access. */
+int fp8mot_mfma_ceiling(const uint8_t* a, int64_t na, const uint8_t* b, int64_t nb,
+                        int64_t iters, int accum, float* sink, double* flops,
+                        hipStream_t stream);
+
 /* ------------------------------------------------------------------ */
 /* Steps of the hot path                                               */
 /* ------------------------------------------------------------------ */

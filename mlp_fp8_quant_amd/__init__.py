@@ -15,5 +15,6 @@ from .api import (ACC_EXACT, ACC_FP8_MFMA, OBS_MAX,  # noqa: F401
                   fp8_observe,
                   fp8_observe_swiglu, fp8_quant_static, fp8_scale_from_state,
                   gated_mlp_fp8, gated_mlp_fp8_noalloc, gated_mlp_fp8_workspace, init,
+                  mfma_ceiling,
                   new_observer_state, qkv_fp8, qkv_fp8_workspace, rtn_weight, rw_ceiling,
                   silu_mul_2in_fp8, silu_mul_fp8)

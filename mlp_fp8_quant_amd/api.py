@@ -430,6 +430,21 @@ def rw_ceiling(a, b, out):
     return out
 
 
+def mfma_ceiling(a, b, iters, sink, accum=ACC_EXACT):
+    """Measurement aid: 8 * iters dense MFMAs per wave on fragments built from
+    the E4M3 codes in a and b (uint8 GPU tensors, indices wrapped), with
+    nothing else in the loop; accum selects the F16 (exact engine) or the
+    native FP8 instruction.  sink: one float32 GPU element, written only if
+    the products sum to a sentinel.  Returns the launch's FLOP count."""
+    _need(a, "a", torch.uint8)
+    _need(b, "b", torch.uint8, a.device)
+    _need(sink, "sink", torch.float32, a.device)
+    flops = ctypes.c_double(0.0)
+    _lib.call("fp8mot_mfma_ceiling", _ptr(a), a.numel(), _ptr(b), b.numel(), int(iters),
+              int(accum), _ptr(sink), ctypes.byref(flops), _stream(a))
+    return flops.value
+
+
 def debug_quant_launches():
     return int(_lib.lib().fp8mot_debug_quant_launches())
 

@@ -143,6 +143,20 @@ int fp8mot_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_
   return hip_status(launch_rw_ceiling(a, b, out, n, ew_blocks(cus), stream));
 }
 
+int fp8mot_mfma_ceiling(const uint8_t* a, int64_t na, const uint8_t* b, int64_t nb,
+                        int64_t iters, int accum, float* sink, double* flops,
+                        hipStream_t stream) {
+  if (a == nullptr || b == nullptr || sink == nullptr || flops == nullptr || na < 64 ||
+      nb < 64 || iters < 1)
+    return FP8MOT_ERR_INVALID_ARG;
+  if (accum != FP8MOT_ACC_EXACT && accum != FP8MOT_ACC_FP8_MFMA) return FP8MOT_ERR_INVALID_ARG;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  *flops = mfma_ceiling_flops(cus, iters, accum);
+  return hip_status(launch_mfma_ceiling(a, na, b, nb, iters, accum, sink, cus, stream));
+}
+
 int fp8_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                      const float* d_scale, hipStream_t stream) {
   if (d_scale == nullptr) return FP8MOT_ERR_UNSUPPORTED;

@@ -43,6 +43,16 @@ hipError_t launch_silu_mul_adjacent(const uint16_t* x, uint8_t* q, int64_t rows,
 hipError_t launch_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_t n,
                              int max_blocks, hipStream_t stream);
 
+// Measurement aid: dense MFMAs on fragments built from the code buffers a [na]
+// and b [nb] (na, nb >= 64; indices wrapped), 8 * iters per wave, engine 0 F16 on decoded
+// codes, 1 native FP8; mfma_ceiling_grid(num_cus) workgroups of 512 threads (one per CU).
+// sink: one float, written only if the products sum to a sentinel.
+int mfma_ceiling_grid(int num_cus);
+double mfma_ceiling_flops(int num_cus, int64_t iters, int engine);
+hipError_t launch_mfma_ceiling(const uint8_t* a, int64_t na, const uint8_t* b, int64_t nb,
+                               int64_t iters, int engine, float* sink, int num_cus,
+                               hipStream_t stream);
+
 // u == nullptr: amax of the BF16 tensor x; otherwise amax of silu(x) * u.
 hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,
                           fp8mot_observer_state_dev* st, int mode, float c,

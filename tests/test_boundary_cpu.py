@@ -98,6 +98,17 @@ def test_refusals_before_any_device_access():
     assert lib.fp8_quant_static(null, fake, 16, s, null) == 1
     # empty tensors are a valid no-op
     assert lib.fp8_quant_static(null, null, 0, s, null) == 0
+    # the MFMA-ceiling measurement aid: NULL pointers, buffers under 64 codes,
+    # no iterations or another engine -> INVALID_ARG
+    flops = ctypes.c_double(0.0)
+    fl = ctypes.byref(flops)
+    assert lib.fp8mot_mfma_ceiling(null, 64, fake, 64, 1, 0, fake, fl, null) == 1
+    assert lib.fp8mot_mfma_ceiling(fake, 64, fake, 64, 1, 0, null, fl, null) == 1
+    assert lib.fp8mot_mfma_ceiling(fake, 64, fake, 64, 1, 0, fake, None, null) == 1
+    assert lib.fp8mot_mfma_ceiling(fake, 63, fake, 64, 1, 0, fake, fl, null) == 1
+    assert lib.fp8mot_mfma_ceiling(fake, 64, fake, 63, 1, 1, fake, fl, null) == 1
+    assert lib.fp8mot_mfma_ceiling(fake, 64, fake, 64, 0, 0, fake, fl, null) == 1
+    assert lib.fp8mot_mfma_ceiling(fake, 64, fake, 64, 1, 2, fake, fl, null) == 1
     assert lib.fp8_linear(null, null, null, 0, 4, 16, s, s, 0, null, 0, null) == 0
     # misaligned base pointers -> MISALIGNED
     assert lib.fp8_quant_static(odd, fake, 16, s, null) == 2

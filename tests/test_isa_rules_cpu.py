@@ -63,3 +63,43 @@ def test_vector_stores_and_mfma_present(assembly):
     gemm = assembly["gemm.hip"]
     assert any(re.match(r"^\s*v_mfma_", l) for l in gemm)
     assert any(re.match(r"^\s*buffer_store_", l) for l in gemm)
+
+
+def _kernels(lines):
+    """Kernel name -> its assembly lines (from its label to .Lfunc_end)."""
+    out, name = {}, None
+    for l in lines:
+        m = re.match(r"^(_Z\S*):", l)
+        if m:
+            name = m.group(1)
+            out[name] = []
+        elif name is not None:
+            if l.startswith(".Lfunc_end"):
+                name = None
+            else:
+                out[name].append(l)
+    return out
+
+
+@pytest.mark.parametrize("engine,mnemonic", [(0, "v_mfma_f32_32x32x16_f16"),
+                                             (1, "v_mfma_f32_32x32x64_f8f6f4")])
+def test_mfma_ceiling_loop_keeps_its_mfmas(assembly, engine, mnemonic):
+    """The measurement loop of fp8mot_mfma_ceiling issues its eight MFMAs per
+    iteration inside one backward branch, and nothing spills: the compiler
+    dropped none of the work the benchmark counts."""
+    ks = {k: v for k, v in _kernels(assembly["mfma_ceiling.hip"]).items()
+          if "mfma_ceiling_kernel" in k and f"ILi{engine}E" in k}
+    assert len(ks) == 1, list(ks)
+    body = next(iter(ks.values()))
+    assert not any("scratch_" in l for l in body)
+    found = False
+    for i, l in enumerate(body):
+        m = re.match(r"^(\.LBB\w+):", l)
+        if not m:
+            continue
+        for j in range(i + 1, len(body)):
+            if re.match(rf"^\s*s_cbranch_\w+\s+{re.escape(m.group(1))}\b", body[j]):
+                n = sum(1 for x in body[i:j] if x.strip().startswith(mnemonic))
+                found |= n == 8
+                break
+    assert found
