@@ -67,13 +67,15 @@ def time_launches(torch, stream, f, reps, warm=2):
 
 
 def mfma_ceiling_against(fp8, torch, stream, kernel, flops, a, b, accum, rounds=3,
-                         window_s=0.3):
+                         window_s=0.3, clock=None):
     """A GEMM kernel beside the MFMA ceiling on the same operand codes: the
     library's dense MFMA loop (fp8mot_mfma_ceiling; fragments taken from the
     codes in a and b, nothing else in the loop) sized to last about as long
     as one kernel launch, the two timed alternately `rounds` times in
     windows of ~window_s each (so both run in the same power and clock
-    state); medians.  kernel(r) launches the GEMM, which does `flops`."""
+    state); medians.  kernel(r) launches the GEMM, which does `flops`.  With a
+    ClockSampler, the GFX clock is also sampled over ~1.5 s of sustained
+    ceiling launches."""
     sink = torch.zeros(1, dtype=torch.float32, device=a.device)
     probe_iters = 1000
     t_probe = time_launches(torch, stream,
@@ -88,13 +90,22 @@ def mfma_ceiling_against(fp8, torch, stream, kernel, flops, a, b, accum, rounds=
         cs.append(time_launches(torch, stream,
                                 lambda r: fp8.mfma_ceiling(a, b, iters, sink, accum), reps, warm=1))
     k, c = sorted(ks)[rounds // 2], sorted(cs)[rounds // 2]
+    sclk = None
+    if clock is not None:
+        clock.start()
+        t_end = time.perf_counter() + 1.5
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                fp8.mfma_ceiling(a, b, iters, sink, accum)
+            torch.cuda.synchronize()
+        sclk = clock.stop()
     torch.cuda.synchronize()
     assert float(sink.item()) == 0.0
     ceiling = per_launch / c / 1e6
     achieved = flops / k / 1e6
     return {"ceiling_TFLOP/s": ceiling, "ceiling_launch_us": c, "ceiling_iters": iters,
             "kernel_TFLOP/s_same_windows": achieved, "kernel_launch_us_same_windows": k,
-            "frac_of_ceiling": achieved / ceiling}
+            "frac_of_ceiling": achieved / ceiling, "sclk_during_ceiling": sclk}
 
 
 class ClockSampler:
@@ -313,7 +324,7 @@ def main():
         "kind": "dense v_mfma_f32_32x32x16_f16 loop on fragments of the step's own X and W_gate "
                 "codes (fp8mot_mfma_ceiling), timed alternately with the kernel",
         **mfma_ceiling_against(fp8, torch, stream, fused_call, fused_flops, qxb, q["gate"],
-                               fp8.ACC_EXACT)}
+                               fp8.ACC_EXACT, clock=clock)}
 
     # the native FP8 MFMA engine, same workload (context only)
     ms8 = timed_steps(fp8.ACC_FP8_MFMA, max(args.steps // 2, 5), 3)
