@@ -128,14 +128,16 @@ __device__ __forceinline__ v4i make_rsrc_words(const void* base, int64_t bytes) 
 // which cannot tell which stage buffer a copy writes, does not make every
 // LDS read wait for every copy; the kernel waits for its copies itself
 // (s_waitcnt vmcnt) before the barrier that publishes a stage.  M0 holds the
-// LDS address; one wait state separates its write from the copy.
-__device__ __forceinline__ void copy_to_lds(v4i rsrc, uint32_t lds_addr, int voff) {
+// LDS address; one wait state separates its write from the copy.  The
+// memory address is the descriptor's base + soff (one value for the wave)
+// + voff (per lane).
+__device__ __forceinline__ void copy_to_lds(v4i rsrc, uint32_t lds_addr, int voff, int soff) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
       :
-      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
       : "memory", "m0");
 }
 
@@ -272,7 +274,12 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
   const int kg = KSPL == 1 ? 0 : wave_id / NW;    // K group
   const int wave = wave_id - kg * NW;             // wave within its K group
   const int wm = wave / WN, wn = wave % WN;
-  auto stage_buf = [&](int b) -> uint8_t* { return smem + (kg * NB + b) * STAGE; };
+  // LDS of K group kg: its NB A stages, then its NB B stages, so that every
+  // fragment read is a per-lane base plus an offset that fits the LDS
+  // instruction's 16-bit immediate
+  constexpr int A_STAGE = BM * KS, B_STAGE = BN * KS;
+  auto a_buf = [&](int b) -> uint8_t* { return smem + kg * NB * STAGE + b * A_STAGE; };
+  auto b_buf = [&](int b) -> uint8_t* { return smem + kg * NB * STAGE + NB * A_STAGE + b * B_STAGE; };
   // K group kg's local stage t is the tile's stage t * KSPL + kg
   auto gstage = [&](int t) { return t * KSPL + kg; };
   // A tile's place in the grid: its output rows from m0 and columns from n0
@@ -341,17 +348,33 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
       gkc[i] = c * 16;
     }
   };
-  // copy i of this wave for stage s into buffer b
-  auto issue_copy = [&](const Windows& w, const int* goff, const int* gkc, int b, int s, int i) {
+  // Copy i of this wave for stage s into buffer b.  When K is a multiple of
+  // the stage (KFULL), every stage lies wholly inside K or wholly past it and
+  // a copy needs no per-lane arithmetic: the lane's offset within the first
+  // stage goes in as is and the stage's column offset k0 as the wave's scalar
+  // offset, so a row inside the window reads row * K + k0 + chunk, inside the
+  // window, and a row past it keeps kOOB, past every window however the
+  // range check treats the scalar offset (kOOB + k0 stays below 2^32); a
+  // stage past the end of K reads through an empty descriptor, so nothing is
+  // read and zeros land in LDS.  Otherwise each chunk is checked against K.
+  auto issue_copy = [&](const Windows& w, const int* goff, const int* gkc, int b, int s, int i,
+                        auto kfull) {
     const int k0 = s * KS;
     const int q = wave * LPW + i;
     const v4i rs = q < A_INS ? w.a : ((FUSED && (((q - A_INS) * RPI) & 32)) ? w.b2 : w.b);
-    const int off = (goff[i] != kOOB && k0 + gkc[i] < K) ? goff[i] + k0 : kOOB;
-    copy_to_lds(rs, (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)(stage_buf(b) + q * 1024)), off);
+    const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(
+        (lds_ptr_t)(q < A_INS ? a_buf(b) + q * 1024 : b_buf(b) + (q - A_INS) * 1024));
+    if constexpr (decltype(kfull)::value) {
+      copy_to_lds(k0 < K ? rs : (v4i){0, 0, 0, 0x00020000}, dst, goff[i], k0);
+    } else {
+      const int off = (goff[i] != kOOB && k0 + gkc[i] < K) ? goff[i] + k0 : kOOB;
+      copy_to_lds(rs, dst, off, 0);
+    }
   };
-  auto issue_stage = [&](const Windows& w, const int* goff, const int* gkc, int b, int s) {
+  auto issue_stage = [&](const Windows& w, const int* goff, const int* gkc, int b, int s,
+                         auto kfull) {
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) issue_copy(w, goff, gkc, b, s, i);
+    for (int i = 0; i < LPW; ++i) issue_copy(w, goff, gkc, b, s, i, kfull);
   };
   // local stages per K group (group 1 of an odd count runs one past the end
   // of K, on zeros, so that both groups meet the same barriers)
@@ -367,6 +390,11 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
   // Exact-engine tiles only: the FP8 engine's loop keeps more registers live
   // and would spill in a tile loop, so its workgroups take one tile each.
   constexpr bool PERSIST = ENGINE == 0 && KSPL == 1;
+  // The tile loop, compiled twice: for K a multiple of the stage (copies
+  // without per-lane arithmetic) and for any other K.  The choice is made
+  // once, here: a branch inside the loop would make the register allocator
+  // spill.
+  auto tiles_loop = [&](auto kfull) {
   bool staged = false;
   for (int tile = blockIdx.x, iter = 0; PERSIST ? tile < ntiles : iter < 1;
        tile += gridDim.x, ++iter) {
@@ -391,8 +419,29 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  auto chunk = [&](const uint8_t* base, int r, int c) -> v4i {
-    return *reinterpret_cast<const v4i*>(base + r * KS + (swz(r, c) << 4));
+  // Per-lane LDS bases of the chunks a lane reads, one per chunk slot k of a
+  // stage (F16 engine: step k reads logical chunk 2k + lane/32; FP8 engine:
+  // step k/2 reads chunks 4(k/2) + 2(lane/32) and the next one), for the
+  // lane's row in its wave's first A and B block of stage 0.  A row's
+  // swizzle depends only on the row's bits 1..3, which blocks 32 rows apart
+  // share, so block i of A (j of B) in stage b is base + b * A_STAGE +
+  // i * 32 * KS (+ b * B_STAGE + j * 32 * KS): an immediate offset.  Opaque
+  // to the compiler, so that it keeps these sums instead of re-forming them.
+  constexpr int NSLOT = 4;
+  int lds_a[NSLOT], lds_b[NSLOT];
+  {
+    const int l31 = lane & 31, half = lane >> 5;
+    const int ra = wm * WTM + l31, rb = wn * WTN + l31;
+#pragma unroll
+    for (int k = 0; k < NSLOT; ++k) {
+      const int c = ENGINE == 0 ? 2 * k + half : 4 * (k >> 1) + 2 * half + (k & 1);
+      lds_a[k] = (int)(a_buf(0) - smem) + ra * KS + (swz(ra, c) << 4);
+      lds_b[k] = (int)(b_buf(0) - smem) + rb * KS + (swz(rb, c) << 4);
+      asm volatile("" : "+v"(lds_a[k]), "+v"(lds_b[k]));
+    }
+  }
+  auto chunk_at = [&](int base, int imm) -> v4i {
+    return *reinterpret_cast<const v4i*>(smem + base + imm);
   };
   // K-steps per stage.  FP8 engine: one step of 64 K, a lane reading two
   // chunks (32 codes) per operand.  F16 engine: two steps of 32 K, a lane
@@ -405,26 +454,22 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
   typedef typename std::conditional<ENGINE == 0, v4i, v8i>::type frag_t;
   frag_t fa[2][FM], fb[2][FN];
   auto rd = [&](int b, int st, int slot) {   // fragments of step st of the stage in buffer b
-    const uint8_t* sa = stage_buf(b);
-    const uint8_t* sb = sa + BM * KS;
     if constexpr (ENGINE == 0) {
-      const int c = 2 * st + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa[slot][i] = chunk(sa, wm * WTM + i * 32 + (lane & 31), c);
+      for (int i = 0; i < FM; ++i) fa[slot][i] = chunk_at(lds_a[st], b * A_STAGE + i * 32 * KS);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb[slot][j] = chunk(sb, wn * WTN + j * 32 + (lane & 31), c);
+      for (int j = 0; j < FN; ++j) fb[slot][j] = chunk_at(lds_b[st], b * B_STAGE + j * 32 * KS);
     } else {
-      const int c = 4 * st + 2 * (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 32 + (lane & 31);
-        fa[slot][i] = __builtin_shufflevector(chunk(sa, r, c), chunk(sa, r, c + 1), 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      for (int i = 0; i < FM; ++i)
+        fa[slot][i] = __builtin_shufflevector(chunk_at(lds_a[2 * st], b * A_STAGE + i * 32 * KS),
+                                              chunk_at(lds_a[2 * st + 1], b * A_STAGE + i * 32 * KS),
+                                              0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WTN + j * 32 + (lane & 31);
-        fb[slot][j] = __builtin_shufflevector(chunk(sb, r, c), chunk(sb, r, c + 1), 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      for (int j = 0; j < FN; ++j)
+        fb[slot][j] = __builtin_shufflevector(chunk_at(lds_b[2 * st], b * B_STAGE + j * 32 * KS),
+                                              chunk_at(lds_b[2 * st + 1], b * B_STAGE + j * 32 * KS),
+                                              0, 1, 2, 3, 4, 5, 6, 7);
     }
     // keep the reads ahead of the MFMAs that follow, so that their latency
     // is covered by this step's matrix work
@@ -465,7 +510,7 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
         if constexpr (kCopies) {
 #pragma unroll
           for (int c = 0; c < CPR; ++c)
-            if (i * CPR + c < LPW) issue_copy(win, goff, gkc, cb, cs, i * CPR + c);
+            if (i * CPR + c < LPW) issue_copy(win, goff, gkc, cb, cs, i * CPR + c, kfull);
         }
       }
     } else {
@@ -478,7 +523,7 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
         if constexpr (kCopies) {
 #pragma unroll
           for (int c = 0; c < CPR; ++c)
-            if (i * CPR + c < LPW) issue_copy(win, goff, gkc, cb, cs, i * CPR + c);
+            if (i * CPR + c < LPW) issue_copy(win, goff, gkc, cb, cs, i * CPR + c, kfull);
         }
       }
     }
@@ -512,7 +557,7 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
   if (!staged) {
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      if (u < KT) issue_stage(win, goff, gkc, u, gstage(u));
+      if (u < KT) issue_stage(win, goff, gkc, u, gstage(u), kfull);
   }
   if (KT > 0) {
     // staged: the previous epilogue's stores were issued after these copies
@@ -596,7 +641,7 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
     copy_offsets(nt, ngoff, ngkc);
 #pragma unroll
     for (int u = 0; u < NB; ++u)
-      if (u < KT) issue_stage(nw, ngoff, ngkc, u, gstage(u));
+      if (u < KT) issue_stage(nw, ngoff, ngkc, u, gstage(u), kfull);
     staged = true;
   }
 
@@ -755,6 +800,11 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
       }
   }
   }  // tile loop
+  };
+  if (K % KS == 0)
+    tiles_loop(std::true_type{});
+  else
+    tiles_loop(std::false_type{});
 }
 
 // Launches one GEMM kernel: one workgroup per tile, or -- for the exact
