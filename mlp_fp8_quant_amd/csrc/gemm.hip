@@ -188,8 +188,10 @@ __device__ __forceinline__ void quad_transpose_halves(uint32_t a, uint32_t b, in
 }
 
 // Operand staging: a stage covers KS = 128 of K.  Its LDS rows hold the 128
-// FP8 codes of one A or B row (A rows first, then B rows), and NB stages
-// live in LDS at once (two, or with DEEP as many as fit, up to four).  The
+// FP8 codes of one A or B row, and NB stages live in LDS at once (two, or
+// with DEEP as many as fit, up to four): the NB A stages first, then the NB
+// B stages, so that a fragment read is a per-lane base plus an offset that
+// fits the LDS instruction's immediate.  The
 // global -> LDS copy is done by the buffer unit itself (buffer_load_dwordx4
 // with the LDS flag): one wave-wide instruction fills 1 KB of a stage (8
 // rows) -- lane i's 16 bytes land at byte 16*i -- with no registers in
