@@ -262,15 +262,18 @@ def test_refusals():
 
 
 @pytest.mark.parametrize("accum", ENGINES)
-def test_many_tiles_ragged_edges_and_k_tail(accum):
+@pytest.mark.parametrize("K", [1040, 1024])
+def test_many_tiles_ragged_edges_and_k_tail(accum, K):
     # more 256x256 tiles than the GPU holds at once (18 x 17 = 306), so the
     # exact engine's workgroups walk several tiles each, with ragged last
-    # tile rows and columns and a K that is not a multiple of the 128-K stage;
-    # every sampled output (the last rows and columns included) against the
-    # exact sum
+    # tile rows and columns and a K that is not a multiple of the 128-K stage
+    # (every chunk checked against K) or is one (whole-stage copies with the
+    # stage's column offset as the scalar offset, rows past M and N reading
+    # zeros); every sampled output (the last rows and columns included)
+    # against the exact sum
     dev = device()
-    M, N, K = 4357, 4136, 1040
-    rng = np.random.default_rng(77 + accum)
+    M, N = 4357, 4136
+    rng = np.random.default_rng(77 + accum + K)
     qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
     sx, sw = np.float32(0.0213), np.float32(1.7e-4)
     out = _run(qa, qb, sx, sw, dev, accum=accum)

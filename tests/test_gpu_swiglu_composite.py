@@ -298,15 +298,18 @@ def test_qkv_grouped_launch_equals_separate_gemms(ns, accum):
 
 
 @pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
-def test_fused_many_tiles_ragged_equals_parts(accum):
+@pytest.mark.parametrize("H", [1040, 1024])
+def test_fused_many_tiles_ragged_equals_parts(accum, H):
     # 18 x 33 = 594 fused tiles (more than the GPU holds at once: the exact
     # engine's workgroups walk several, prefetching the next tile's first
-    # stages during each epilogue), ragged M and I, K not a multiple of 128:
-    # bitwise the separate gate/up GEMMs + SwiGLU, and the codes of sampled
-    # rows (the last ones included) against the oracle
+    # stages during each epilogue), ragged M and I, K not a multiple of 128
+    # (every chunk checked against K) or a multiple of it (whole-stage copies
+    # with the stage's column offset as the scalar offset, rows past M and I
+    # reading zeros): bitwise the separate gate/up GEMMs + SwiGLU, and the
+    # codes of sampled rows (the last ones included) against the oracle
     dev = device()
-    M, I, H = 4357, 4144, 1040
-    rng = np.random.default_rng(88 + accum)
+    M, I = 4357, 4144
+    rng = np.random.default_rng(88 + accum + H)
     x = workloads.activations(rng, M, H)
     wg = workloads.weights(rng, I, H, 0.02)
     wu = workloads.weights(rng, I, H, 0.02)
