@@ -69,6 +69,7 @@ STATUS = {
 }
 
 _lib = None
+_funcs = {}
 
 
 class Fp8motError(RuntimeError):
@@ -99,8 +100,10 @@ def lib():
 
 def call(name, *args):
     """Call an int-returning entry point; raise Fp8motError on failure."""
-    l = lib()
-    st = getattr(l, name)(*args)
+    f = _funcs.get(name)
+    if f is None:
+        f = _funcs[name] = getattr(lib(), name)
+    st = f(*args)
     if st != 0:
-        raise Fp8motError(name, st, l.fp8mot_status_string(st).decode())
+        raise Fp8motError(name, st, lib().fp8mot_status_string(st).decode())
     return st

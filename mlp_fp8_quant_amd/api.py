@@ -25,12 +25,21 @@ OBS_MAX, OBS_MOVING_AVG = 0, 1
 _OUT_DTYPE = {OUT_BF16: torch.bfloat16, OUT_FP8: torch.uint8, OUT_F32: torch.float32}
 
 
+# Host cost per call matters for the small, latency-bound launches: the raw
+# handle of the device's current stream (the capture stream under graph
+# capture) is taken without building a Stream object, and pointers go to
+# ctypes as plain integers (None for NULL).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    return t.data_ptr() if t is not None else None
 
 
 def _need(t, name, dtype, device=None):
