@@ -258,14 +258,15 @@ __global__ __launch_bounds__(WM* WN * 64 * KSPL, 1) void gemm_kernel(GemmArgs g)
   constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;   // 32x32 blocks per wave
   constexpr int STAGE = (BM + BN) * KS;
-  // stages resident in LDS: two, or with DEEP as many as the 160 KB hold, up
-  // to four (two for 256x256 tiles, three for 256x128, four for 128x128)
-  constexpr int NB = !DEEP ? 2 : (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;
+  // stages resident in LDS per K group: two, or with DEEP as many as the
+  // 160 KB hold, up to four (two for 256x256 tiles, three for 256x128, four
+  // for 128x128; three for 128x64 with the K split's two groups)
+  constexpr int NB = !DEEP ? 2 : (160 * 1024) / (KSPL * STAGE) < 4 ? (160 * 1024) / (KSPL * STAGE) : 4;
   constexpr int A_INS = BM / RPI, INS = (BM + BN) / RPI;   // wave-wide copies per stage
   constexpr int LPW = INS / NW;                            // ... per wave
   static_assert(LPW * NW == INS, "tile rows / waves");
   static_assert(!FUSED || (BN == 256 && FN % 2 == 0), "fused tiles pair gate/up blocks");
-  static_assert(KSPL == 1 || (KSPL == 2 && !FUSED && !DEEP), "K split: plain tiles, two stages");
+  static_assert(KSPL == 1 || (KSPL == 2 && !FUSED), "K split: plain tiles");
   static_assert(KSPL * NB * STAGE <= 160 * 1024, "stages fit the 160 KB LDS of a CU");
   static_assert(KSPL == 1 || NW * FM * FN * 16 * 64 * 4 <= KSPL * NB * STAGE,
                 "the K groups' sums fit the stage buffers");
@@ -906,7 +907,10 @@ template <int BM, int BN, int WM, int WN, int ENGINE>
 hipError_t launch_cfg(GemmArgs a, int out_kind, int num_cus, hipStream_t stream, bool split) {
   set_tiles<BM, BN>(a);
   if constexpr (BM == 128) {
-    if (split) return launch_tiled<BM, BN, WM, WN, ENGINE, false, 2>(a, out_kind, num_cus, stream);
+    // 128x64 tiles leave room for three stages per K group (measured on the
+    // und tower's 512x4096x12288 down projection, whose copies the two-stage
+    // loop waits on)
+    if (split) return launch_tiled<BM, BN, WM, WN, ENGINE, BN == 64, 2>(a, out_kind, num_cus, stream);
   }
   const bool deep = ENGINE == 1 && (BM + BN > 256 || (int64_t)a.tiles_m * a.tiles_n <= num_cus);
   if (deep) return launch_tiled<BM, BN, WM, WN, ENGINE, true, 1>(a, out_kind, num_cus, stream);
