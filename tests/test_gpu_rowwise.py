@@ -31,7 +31,8 @@ def _quant_dev(x, dev):
     return host_u8(q), host_f32(s)
 
 
-@pytest.mark.parametrize("rows,K", [(1, 16), (17, 2048), (300, 5120), (64, 25600), (3, 48), (5, 32784)])
+@pytest.mark.parametrize("rows,K", [(1, 16), (17, 2048), (33, 4096), (300, 5120), (7, 6160),
+                                    (9, 8192), (64, 25600), (3, 48), (5, 32784)])
 def test_quant_per_row_bitexact(rows, K):
     dev = device()
     x = _rows(np.random.default_rng(rows * 7 + K), rows, K)
