@@ -885,13 +885,24 @@ int forced_env(const char* name) {
 // 256x256 tiles with 8 waves (two per SIMD) are fastest once there are
 // ~0.7 tiles per CU; below that 256x128 (8 waves), then 128x128 and 128x64
 // (4 waves; 512x4096x4096: 33.9 -> 25.8 us, 512x4096x12288: 72.7 -> 55.6 us
-// with 128x64) keep the CUs busy.  FP8MOT_GEMM_CFG=<1|5|3|6> forces one
-// configuration (tuning; 6 is 128x64).
-int pick_cfg(int64_t tiles_256x256, int64_t tiles_256x128, int64_t tiles_128x128, int num_cus) {
+// with 128x64) keep the CUs busy.  Where 256x256 tiles are used, 192x256
+// tiles (8 waves of 96x64) replace them when they fill the rounds of one
+// workgroup per CU better: both run one workgroup per CU, and a 192x256 tile
+// takes ~0.92 of a 256x256 tile's time, so the rounds are compared at that
+// weight (split Q/K/V, 3072 x 3*4096 x 4096: 576 tiles of 256x256 are 2.25
+// per CU, 768 of 192x256 exactly 3; 298.5 -> 273.2 us, and 185.6 -> 163.9 us
+// for 1536 rows).  FP8MOT_GEMM_CFG=<1|5|3|6|7> forces one configuration
+// (tuning; 6 is 128x64, 7 is 192x256).
+int pick_cfg(int64_t tiles_256x256, int64_t tiles_192x256, int64_t tiles_256x128,
+             int64_t tiles_128x128, int num_cus) {
   static const int forced = forced_env("FP8MOT_GEMM_CFG");
-  if (forced >= 0) return forced == 1 || forced == 5 || forced == 6 ? forced : 3;
+  if (forced >= 0) return forced == 1 || forced == 5 || forced == 6 || forced == 7 ? forced : 3;
   const int64_t want = (int64_t)num_cus * 7 / 10;
-  if (tiles_256x256 >= want) return 1;
+  if (tiles_256x256 >= want) {
+    const int64_t r256 = (tiles_256x256 + num_cus - 1) / num_cus;
+    const int64_t r192 = (tiles_192x256 + num_cus - 1) / num_cus;
+    return r192 * 92 < r256 * 100 ? 7 : 1;
+  }
   if (tiles_256x128 >= want) return 5;
   return tiles_128x128 >= want ? 3 : 6;
 }
@@ -928,10 +939,11 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
     }
     return (int64_t)((a.M + bm - 1) / bm) * tn;
   };
-  const int cfg = pick_cfg(tiles(256, 256), tiles(256, 128), tiles(128, 128), num_cus);
+  const int cfg = pick_cfg(tiles(256, 256), tiles(192, 256), tiles(256, 128), tiles(128, 128), num_cus);
   const bool split = a.groups == 1 && gemm_splits_k(a.M, a.N, a.K, num_cus, ENGINE);
   switch (cfg) {
     case 1: return launch_cfg<256, 256, 2, 4, ENGINE>(a, out_kind, num_cus, stream, false);
+    case 7: return launch_cfg<192, 256, 2, 4, ENGINE>(a, out_kind, num_cus, stream, false);
     case 5: return launch_cfg<256, 128, 4, 2, ENGINE>(a, out_kind, num_cus, stream, false);
     case 6: return launch_cfg<128, 64, 2, 2, ENGINE>(a, out_kind, num_cus, stream, split);
     default: return launch_cfg<128, 128, 2, 2, ENGINE>(a, out_kind, num_cus, stream, split);
@@ -943,8 +955,8 @@ hipError_t launch_engine(GemmArgs a, int out_kind, int num_cus, hipStream_t stre
 bool gemm_splits_k(int64_t M, int64_t N, int64_t K, int num_cus, int accum) {
   static const int forced = forced_env("FP8MOT_GEMM_SPLIT");   // 0: never, 1: any K (tuning)
   if (forced == 0 || K <= KS) return false;
-  const int cfg = pick_cfg(tiles_of(M, N, 256, 256), tiles_of(M, N, 256, 128),
-                           tiles_of(M, N, 128, 128), num_cus);
+  const int cfg = pick_cfg(tiles_of(M, N, 256, 256), tiles_of(M, N, 192, 256),
+                           tiles_of(M, N, 256, 128), tiles_of(M, N, 128, 128), num_cus);
   // 128x64 tiles split K for the exact engine only: the FP8 engine's four
   // 24 KB stages in LDS serve it better there (512x4096x12288: 48.1 us split,
   // 41.1 us with four stages), while at 128x128 the split wins for both

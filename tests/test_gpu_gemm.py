@@ -263,17 +263,19 @@ def test_refusals():
 
 @pytest.mark.parametrize("accum", ENGINES)
 @pytest.mark.parametrize("K", [1040, 1024])
-def test_many_tiles_ragged_edges_and_k_tail(accum, K):
-    # more 256x256 tiles than the GPU holds at once (18 x 17 = 306), so the
-    # exact engine's workgroups walk several tiles each, with ragged last
-    # tile rows and columns and a K that is not a multiple of the 128-K stage
-    # (every chunk checked against K) or is one (whole-stage copies with the
-    # stage's column offset as the scalar offset, rows past M and N reading
-    # zeros); every sampled output (the last rows and columns included)
-    # against the exact sum
+@pytest.mark.parametrize("M,N", [(4357, 4136), (4090, 8180)])
+def test_many_tiles_ragged_edges_and_k_tail(accum, K, M, N):
+    # more tiles than the GPU holds at once, so the exact engine's workgroups
+    # walk several tiles each: 4357 x 4136 takes 192x256 tiles (391 of them;
+    # 306 of 256x256 would leave the second round part-filled), 4090 x 8180
+    # takes 256x256 tiles (512, two full rounds); ragged last tile rows and
+    # columns, and a K that is not a multiple of the 128-K stage (every chunk
+    # checked against K) or is one (whole-stage copies with the stage's column
+    # offset as the scalar offset, rows past M and N reading zeros); every
+    # sampled output (the last rows and columns included) against the exact
+    # sum
     dev = device()
-    M, N = 4357, 4136
-    rng = np.random.default_rng(77 + accum + K)
+    rng = np.random.default_rng(77 + accum + K + M)
     qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
     sx, sw = np.float32(0.0213), np.float32(1.7e-4)
     out = _run(qa, qb, sx, sw, dev, accum=accum)
