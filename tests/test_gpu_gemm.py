@@ -137,11 +137,12 @@ def test_fp8_output_epilogue(accum):
 
 @pytest.mark.parametrize("accum", ENGINES)
 @pytest.mark.parametrize("M,N,K", [(257, 385, 1040), (129, 127, 144), (64, 48, 1168),
-                                   (300, 200, 4096), (512, 1024, 512)])
+                                   (300, 200, 4096), (512, 1024, 512), (3000, 6000, 1024)])
 def test_fp8_output_is_the_encoded_f32_output(accum, M, N, K):
     # the FP8 epilogue encodes fp32(acc * alpha) / s_y: bit for bit the
     # encoding (oracle encoder, IEEE FP32 division) of the same kernel's FP32
-    # output, on ragged widths (byte stores) and vector ones alike
+    # output, on ragged widths (byte stores) and vector ones alike; 3000 x
+    # 6000 takes 192x256 tiles (three 32-row blocks per wave)
     dev = device()
     rng = np.random.default_rng(M + 7 * N + K)
     qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))

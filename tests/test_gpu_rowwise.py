@@ -86,6 +86,35 @@ def _check_rowwise_bf16(yb, y32, S, A, alpha):
 
 
 @pytest.mark.parametrize("engine", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+def test_linear_rowwise_192_row_tiles_sampled_rows(engine):
+    # 3000 x 6000 x 1024 takes 192x256 tiles (three 32-row blocks per wave,
+    # ragged last tile row and column): the per-row epilogue on sampled rows,
+    # the last ones included, against the oracle
+    dev = device()
+    M, N, K = 3000, 6000, 1024
+    rng = np.random.default_rng(5 + engine)
+    x = _rows(rng, M, K, 0.05, 20)
+    w = _rows(rng, N, K, 0.002, 0.05)
+    qx_d, sx_d = fp8.fp8_quant_per_row(to_dev_bf16(x.ravel(), dev).view(M, K))
+    qw_d, sw_d = fp8.fp8_quant_per_row(to_dev_bf16(w.ravel(), dev).view(N, K))
+    qw, sw = quant_per_row(w)
+    assert np.array_equal(host_u8(qw_d), qw)
+    rows = np.concatenate([np.arange(M - 40, M), np.sort(rng.choice(M - 40, 24, replace=False))])
+    qx, sx = quant_per_row(x[rows])
+    assert np.array_equal(host_u8(qx_d)[rows], qx)
+    S, A = gemm_exact(qx, qw)
+    alpha = epilogue_rowwise_alpha(sx, sw)
+    y32 = host_f32(fp8.fp8_linear_rowwise(qx_d, qw_d, sx_d, sw_d, out_kind=fp8.OUT_F32, accum=engine))[rows]
+    yb = host_bits(fp8.fp8_linear_rowwise(qx_d, qw_d, sx_d, sw_d, accum=engine))[rows]
+    if engine == fp8.ACC_EXACT:
+        _check_rowwise_f32(y32, S, A, alpha)
+        _check_rowwise_bf16(yb, y32, S, A, alpha)
+    else:
+        check_gemm_fp8_engine(y32[:8], S[:8], A[:8], alpha[:8], fp8_mfma_group_bound(qx[:8], qw))
+        assert np.array_equal(yb, f32_to_bf16(y32))
+
+
+@pytest.mark.parametrize("engine", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
 @pytest.mark.parametrize("M,N,K", [(1, 16, 16), (37, 129, 144), (300, 200, 4096), (257, 385, 1040)])
 def test_linear_rowwise_against_oracle(engine, M, N, K):
     dev = device()
