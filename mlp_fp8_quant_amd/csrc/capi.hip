@@ -299,7 +299,9 @@ int check_gated_mlp(const uint16_t* x, int64_t M, int64_t H, int64_t I, const fl
   // gate/up: K = H, FP8 output rows of I; down: K = I, BF16 output rows of H
   if (!gemm_sizes_ok(M, I, H, I, 1) || !gemm_sizes_ok(M, H, I, H, 2)) return FP8MOT_ERR_INVALID_ARG;
   if (M == 0 || H == 0) return FP8MOT_OK;
-  if (!x || !wg || !wu || !wd || !y) return FP8MOT_ERR_INVALID_ARG;
+  // I == 0: the three weights are empty (their pointers may be NULL) and y is
+  // the down projection of an empty sum, zero
+  if (!x || !y || (I > 0 && (!wg || !wu || !wd))) return FP8MOT_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(wg) || !aligned16(wu) || !aligned16(wd) || !aligned16(y))
     return FP8MOT_ERR_MISALIGNED;
   return FP8MOT_OK;

@@ -121,6 +121,12 @@ def test_refusals_before_any_device_access():
                              fake, null, 0, 0, null) == 6
     assert lib.gated_mlp_fp8(fake, 4, 16, 32, null, fake, s, fake, s, s, fake, s,
                              fake, fake, 1 << 20, 0, null) == 4
+    # I = 0: the weights are empty tensors, NULL allowed; the call gets past
+    # argument validation to the workspace check
+    assert lib.gated_mlp_fp8(fake, 4, 16, 0, s, null, s, null, s, s, null, s,
+                             fake, null, 0, 0, null) == 6
+    assert lib.gated_mlp_fp8(fake, 4, 16, 32, s, null, s, fake, s, s, fake, s,
+                             fake, fake, 1 << 20, 0, null) == 1
     assert lib.fp8_gate_up_swiglu(fake, fake, s, s, fake, s, null, fake, 4, 32, 16, 0, null) == 4
     assert lib.fp8_gate_up_swiglu(fake, fake, s, s, fake, s, s, fake, 4, 24, 16, 0, null) == 1
     assert lib.fp8_gate_up_swiglu(fake, odd, s, s, fake, s, s, fake, 4, 32, 16, 0, null) == 2

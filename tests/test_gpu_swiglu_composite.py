@@ -331,3 +331,39 @@ def test_fused_many_tiles_ragged_equals_parts(accum, H):
     Su, _ = olin.gemm_exact(qx_o[rows], qu)
     want = silu_mul_fp8(olin.epilogue_bf16(Sg, sx, sg), olin.epilogue_bf16(Su, sx, su), sh)
     check_fp8_tolerance(host_u8(qh)[rows].ravel(), want)
+
+
+@pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+def test_degenerate_composite_shapes(accum):
+    # the gated MLP's degenerate shapes, against the oracle chain: no tokens
+    # (M = 0), no intermediate channels (I = 0: the weights are empty tensors
+    # and y is the down projection of an empty sum) and, for the gate/up
+    # half, an empty hidden size (H = 0: G = U = 0, so every SwiGLU code is
+    # that of 0); outputs start as NaN bits so a missing write shows
+    dev = device()
+    M, H, I = 37, 64, 48
+    rng = np.random.default_rng(7 + accum)
+    x = workloads.activations(rng, M, H)
+    dx = to_dev_bf16(x, dev)
+    sx, sg, su, sh, sd = (np.float32(v) for v in (0.02, 0.003, 0.004, 0.05, 0.006))
+    dsx, dsg, dsu, dsh, dsd = (scalar(v, dev) for v in (sx, sg, su, sh, sd))
+    e = lambda *shp: torch.empty(shp, dtype=torch.uint8, device=dev)
+    # M = 0
+    y0 = fp8.gated_mlp_fp8(dx[:0], dsx, e(I, H).zero_(), dsg, e(I, H).zero_(), dsu, dsh,
+                           e(H, I).zero_(), dsd, accum=accum)
+    assert y0.shape == (0, H)
+    # I = 0: y = epilogue of S = 0 (+0 in BF16)
+    qh0 = np.zeros((M, 0), np.uint8)
+    want = olin.epilogue_bf16(olin.gemm_exact(qh0, np.zeros((H, 0), np.uint8))[0], sh, sd)
+    for run in (fp8.gated_mlp_fp8, fp8.gated_mlp_fp8_noalloc):
+        y = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device=dev)
+        run(dx, dsx, e(0, H), dsg, e(0, H), dsu, dsh, e(H, 0), dsd, out=y, accum=accum)
+        assert np.array_equal(host_bits(y), want)
+    # H = 0 for the gate/up half: qh = SwiGLU-FP8 of two zero projections
+    qx0 = np.zeros((M, 0), np.uint8)
+    G = olin.epilogue_bf16(olin.gemm_exact(qx0, np.zeros((I, 0), np.uint8))[0], sx, sg)
+    U = olin.epilogue_bf16(olin.gemm_exact(qx0, np.zeros((I, 0), np.uint8))[0], sx, su)
+    want_qh = silu_mul_fp8(G, U, sh).reshape(M, I)
+    qh = torch.full((M, I), 0x7F, dtype=torch.uint8, device=dev)
+    fp8.fp8_gate_up_swiglu(e(M, 0), e(I, 0), dsx, dsg, e(I, 0), dsu, dsh, out=qh, accum=accum)
+    assert np.array_equal(host_u8(qh), want_qh)
