@@ -30,11 +30,19 @@ _OUT_DTYPE = {OUT_BF16: torch.bfloat16, OUT_FP8: torch.uint8, OUT_F32: torch.flo
 # capture) is taken without building a Stream object, and pointers go to
 # ctypes as plain integers (None for NULL).
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_get_device = getattr(torch._C, "_cuda_getDevice", torch.cuda.current_device)
 
 
 def _stream(t):
+    # the library works on the current HIP device (its CU count and
+    # architecture check come from there): tensors on another device are
+    # refused rather than launched on a stream of the wrong device
+    d = t.get_device()
+    if d != _get_device():
+        raise ValueError(f"tensors are on cuda:{d} but the current device is "
+                         f"cuda:{_get_device()}; call under torch.cuda.device({d})")
     if _raw_stream is not None:
-        return _raw_stream(t.get_device())
+        return _raw_stream(d)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
