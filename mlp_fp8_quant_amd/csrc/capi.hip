@@ -434,13 +434,17 @@ int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
   if (!gemm_sizes_ok(M, Nq + Nk + Nv, H, Nq > Nk ? (Nq > Nv ? Nq : Nv) : (Nk > Nv ? Nk : Nv), 2))
     return FP8MOT_ERR_INVALID_ARG;
   if (M == 0) return FP8MOT_OK;
-  // a member with N == 0 has nothing to read or write (its pointers may be NULL)
-  if (!x || (Nq > 0 && (!wq || !yq)) || (Nk > 0 && (!wk || !yk)) || (Nv > 0 && (!wv || !yv)))
+  // a member with N == 0 has nothing to read or write (its pointers may be
+  // NULL); with H == 0 neither has x nor a member's weight
+  if ((H > 0 && !x) || (Nq > 0 && ((H > 0 && !wq) || !yq)) ||
+      (Nk > 0 && ((H > 0 && !wk) || !yk)) || (Nv > 0 && ((H > 0 && !wv) || !yv)))
     return FP8MOT_ERR_INVALID_ARG;
   if (!aligned16(x) || (Nq > 0 && (!aligned16(wq) || !aligned16(yq))) ||
       (Nk > 0 && (!aligned16(wk) || !aligned16(yk))) || (Nv > 0 && (!aligned16(wv) || !aligned16(yv))))
     return FP8MOT_ERR_MISALIGNED;
-  if (ws == nullptr || !aligned256(ws) || ws_bytes < qkv_fp8_workspace(M, H))
+  // H == 0 needs no workspace (qX is empty)
+  const size_t need = qkv_fp8_workspace(M, H);
+  if (need > 0 && (ws == nullptr || !aligned256(ws) || ws_bytes < need))
     return FP8MOT_ERR_WORKSPACE;
   int cus = 0;
   int st = current_device(&cus);

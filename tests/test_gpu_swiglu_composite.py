@@ -367,3 +367,27 @@ def test_degenerate_composite_shapes(accum):
     qh = torch.full((M, I), 0x7F, dtype=torch.uint8, device=dev)
     fp8.fp8_gate_up_swiglu(e(M, 0), e(I, 0), dsx, dsg, e(I, 0), dsu, dsh, out=qh, accum=accum)
     assert np.array_equal(host_u8(qh), want_qh)
+
+
+@pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+def test_degenerate_qkv_shapes(accum):
+    # qkv_fp8 with an empty hidden size (H = 0: no quantization launch, each
+    # projection the epilogue of an empty sum, +0 in BF16) and with no tokens
+    dev = device()
+    M, ns = 33, (64, 32, 48)
+    s = [np.float32(v) for v in (0.02, 0.003, 0.004, 0.005)]
+    ds = [scalar(v, dev) for v in s]
+    e = lambda *shp: torch.empty(shp, dtype=torch.uint8, device=dev)
+    x0 = torch.empty((M, 0), dtype=torch.bfloat16, device=dev)
+    outs = tuple(torch.full((M, n), float("nan"), dtype=torch.bfloat16, device=dev) for n in ns)
+    before = fp8.debug_quant_launches()
+    fp8.qkv_fp8(x0, ds[0], e(ns[0], 0), ds[1], e(ns[1], 0), ds[2], e(ns[2], 0), ds[3],
+                outs=outs, accum=accum)
+    assert fp8.debug_quant_launches() == before
+    for y, n, sw in zip(outs, ns, s[1:]):
+        S, _ = olin.gemm_exact(np.zeros((M, 0), np.uint8), np.zeros((n, 0), np.uint8))
+        assert np.array_equal(host_bits(y), olin.epilogue_bf16(S, s[0], sw))
+    x = to_dev_bf16(workloads.activations(np.random.default_rng(3), 1, 64), dev)[:0]
+    yq, yk, yv = fp8.qkv_fp8(x, ds[0], e(ns[0], 64).zero_(), ds[1], e(ns[1], 64).zero_(), ds[2],
+                             e(ns[2], 64).zero_(), ds[3], accum=accum)
+    assert (yq.shape, yk.shape, yv.shape) == ((0, 64), (0, 32), (0, 48))
