@@ -253,7 +253,8 @@ int silu_mul_fp8(const uint16_t* x, uint8_t* q, int64_t rows, int64_t inter,
  * tokens) and, at load time, per-channel weights (rows = output channels).
  * K must be a multiple of 16 (FP8MOT_ERR_INVALID_ARG); x, q 16-byte aligned
  * (FP8MOT_ERR_MISALIGNED); d_scales: FP32 [rows], caller-owned device memory.
- * rows == 0 or K == 0 does nothing. */
+ * rows == 0 does nothing; K == 0 writes scale 0 for every row (an empty row
+ * is a zero row) and then x and q may be NULL. */
 int fp8_quant_per_row(const uint16_t* x, uint8_t* q, float* d_scales,
                       int64_t rows, int64_t K, hipStream_t stream);
 

@@ -233,8 +233,10 @@ int fp8_quant_per_row(const uint16_t* x, uint8_t* q, float* d_scales,
                       int64_t rows, int64_t K, hipStream_t stream) {
   if (rows < 0 || K < 0 || (K % 16) != 0) return FP8MOT_ERR_INVALID_ARG;
   if (rows > 0 && K > INT64_MAX / rows) return FP8MOT_ERR_INVALID_ARG;
-  if (rows == 0 || K == 0) return FP8MOT_OK;
-  if (x == nullptr || q == nullptr || d_scales == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (rows == 0) return FP8MOT_OK;
+  // K == 0: empty rows, each a zero row (scale 0); x and q may be NULL
+  if (d_scales == nullptr || (K > 0 && (x == nullptr || q == nullptr)))
+    return FP8MOT_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(q)) return FP8MOT_ERR_MISALIGNED;
   int cus = 0;
   int st = current_device(&cus);

@@ -210,6 +210,8 @@ def test_rowwise_refusals_before_any_device_access():
     assert lib.fp8_quant_per_row(fake, fake, null, 4, 16, null) == 1
     assert lib.fp8_quant_per_row(odd, fake, fake, 4, 16, null) == 2
     assert lib.fp8_quant_per_row(null, null, null, 0, 16, null) == 0
+    # K == 0 still writes one scale per row: the scales must be given
+    assert lib.fp8_quant_per_row(null, null, null, 4, 0, null) == 1
     # per-row GEMM: FP8 output unsupported, NULL scales, bad enums, alignment
     assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, s, s, 1, 0, null) == 4
     assert lib.fp8_linear_rowwise(fake, fake, fake, 4, 4, 16, null, s, 0, 0, null) == 4

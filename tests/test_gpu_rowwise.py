@@ -156,6 +156,17 @@ def test_linear_rowwise_gen_mlp_shape_sampled_rows():
     _check_rowwise_f32(y32[rows], S, A, epilogue_rowwise_alpha(sx, sw))
 
 
+def test_quant_per_row_empty_rows_get_scale_zero():
+    # K = 0: every row is empty, which the oracle scales as a zero row (0);
+    # the scales start as NaN so a missing write shows
+    dev = device()
+    x = torch.empty((5, 0), dtype=torch.bfloat16, device=dev)
+    scales = torch.full((5,), float("nan"), dtype=torch.float32, device=dev)
+    q, s = fp8.fp8_quant_per_row(x, scales=scales)
+    wq, ws = quant_per_row(np.zeros((5, 0), np.uint16))
+    assert q.shape == (5, 0) and np.array_equal(host_f32(s).view(np.uint32), ws.view(np.uint32))
+
+
 def test_rowwise_refusals():
     dev = device()
     q = torch.zeros((4, 32), dtype=torch.uint8, device=dev)

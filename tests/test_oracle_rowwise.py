@@ -86,3 +86,17 @@ def test_rowwise_epilogue_is_the_scaled_dequantized_product():
     yb = bf16_to_f32(epilogue_rowwise_bf16(S, sx, sw)).astype(np.float64)
     full = bf16_to_f32(x).astype(np.float64) @ bf16_to_f32(w).astype(np.float64).T
     assert np.max(np.abs(yb - full)) < 0.08 * np.max(np.abs(full))
+
+
+def test_empty_rows_scale_as_zero_rows():
+    # appending zeros to a row never changes its amax, so an empty row (K = 0)
+    # takes the scale of a zero row of any length: 0
+    _, s_empty = quant_per_row(np.zeros((3, 0), np.uint16))
+    for K in (16, 48):
+        q, s = quant_per_row(np.zeros((3, K), np.uint16))
+        assert np.array_equal(s.view(np.uint32), s_empty.view(np.uint32))
+        assert np.all(q == 0)
+    x = _bf16(np.random.default_rng(4).standard_normal((3, 32)))
+    _, s_x = quant_per_row(x)
+    _, s_pad = quant_per_row(np.concatenate([x, np.zeros((3, 16), np.uint16)], axis=1))
+    assert np.array_equal(s_x.view(np.uint32), s_pad.view(np.uint32))
