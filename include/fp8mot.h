@@ -390,7 +390,9 @@ int qkv_fp8(const uint16_t* x, int64_t M, int64_t H, const float* d_sx,
  *   first call: m = a
  *   FP8MOT_OBS_MAX:        m = max(m, a)            (NaN propagates)
  *   FP8MOT_OBS_MOVING_AVG: m = m + c * (a - m)      (three FP32 roundings, no FMA)
- * x: BF16 [n], n >= 1.  d_state: device fp8mot_observer_state (zero-filled
+ * x: BF16 [n], n >= 1 (an empty call has no maximum to fold, so n == 0 is
+ * FP8MOT_ERR_INVALID_ARG, the one exception to the empty-tensor rule above).
+ * d_state: device fp8mot_observer_state (zero-filled
  * before the first call; 16-byte aligned).  `c` is used by the moving
  * average only and must be finite.  Calls on one state must be
  * stream-ordered. */
