@@ -92,13 +92,7 @@ def mfma_ceiling_against(fp8, torch, stream, kernel, flops, a, b, accum, rounds=
     k, c = sorted(ks)[rounds // 2], sorted(cs)[rounds // 2]
     sclk = None
     if clock is not None:
-        clock.start()
-        t_end = time.perf_counter() + 1.5
-        while time.perf_counter() < t_end:
-            for _ in range(10):
-                fp8.mfma_ceiling(a, b, iters, sink, accum)
-            torch.cuda.synchronize()
-        sclk = clock.stop()
+        sclk = sustained_clock(lambda: fp8.mfma_ceiling(a, b, iters, sink, accum), clock, torch)
     torch.cuda.synchronize()
     assert float(sink.item()) == 0.0
     ceiling = per_launch / c / 1e6
@@ -106,6 +100,29 @@ def mfma_ceiling_against(fp8, torch, stream, kernel, flops, a, b, accum, rounds=
     return {"ceiling_TFLOP/s": ceiling, "ceiling_launch_us": c, "ceiling_iters": iters,
             "kernel_TFLOP/s_same_windows": achieved, "kernel_launch_us_same_windows": k,
             "frac_of_ceiling": achieved / ceiling, "sclk_during_ceiling": sclk}
+
+
+def sustained_clock(fn, clock, torch, seconds=1.5, batch=10):
+    """The GFX clock while fn() runs back to back for ~seconds: batches of
+    launches with the next batch queued before waiting on the previous one,
+    so the GPU never idles while `clock` samples; sampling stops while the
+    last batch is still queued."""
+    clock.start()
+    prev = None
+    t_end = time.perf_counter() + seconds
+    while True:
+        for _ in range(batch):
+            fn()
+        ev = torch.cuda.Event()
+        ev.record()
+        if prev is not None:
+            prev.synchronize()
+        prev = ev
+        if time.perf_counter() >= t_end:
+            break
+    sclk = clock.stop()
+    torch.cuda.synchronize()
+    return sclk
 
 
 class ClockSampler:
@@ -265,13 +282,7 @@ def main():
     ms_step = timed_steps(fp8.ACC_EXACT, args.steps, args.warmup)
     value = gemm_flops / (ms_step * 1e-3) / 1e12
     # the clock under this load: the same step, sustained for ~1.5 s
-    clock.start()
-    t_end = time.perf_counter() + 1.5
-    while time.perf_counter() < t_end:
-        for _ in range(10):
-            step(fp8.ACC_EXACT)
-        torch.cuda.synchronize()
-    sclk_step = clock.stop()
+    sclk_step = sustained_clock(lambda: step(fp8.ACC_EXACT), clock, torch)
 
     # kernels of the step, each timed alone: back-to-back launches on the
     # stream they run on, one pair of HIP events around them
