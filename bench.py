@@ -793,8 +793,14 @@ def cpu_baseline(wl, rows, channels):
     H = x.shape[1]
     flops = 2.0 * rows * C * H * 3
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": dt,
+            "kind": "oracle", "seconds": dt, "cpu_model": cpu_model,
             "sample": f"rows 0..{rows - 1} of X [{wl.x.shape[0]}, {H}] x intermediate "
                       f"channels 0..{C - 1} of {wl.weights['gate'].shape[0]} through the whole "
                       f"gated MLP ({flops / 1e9:.0f} GFLOP); float64 exact GEMMs, "
