@@ -66,6 +66,23 @@ def time_launches(torch, stream, f, reps, warm=2):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def launch_stats(torch, stream, f, reps, warm=2):
+    """Median and minimum per-launch time in microseconds of `reps`
+    back-to-back calls f(r): an event recorded on `stream` between
+    consecutive calls, no host synchronization between them."""
+    for r in range(warm):
+        f(r)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for r in range(reps):
+        f(r)
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps))
+    return {"us_median": d[reps // 2], "us_min": d[0], "launches": reps}
+
+
 def mfma_ceiling_against(fp8, torch, stream, kernel, flops, a, b, accum, rounds=3,
                          window_s=0.3, clock=None):
     """A GEMM kernel beside the MFMA ceiling on the same operand codes: the
@@ -297,13 +314,14 @@ def main():
                 qxb, q["gate"], sx, s["gate"], q["up"], s["up"], sh, out=qh, accum=accum),
             "down": lambda r: fp8.fp8_linear(qh, q["down"], sh, s["down"], out=y, accum=accum),
         }
-        out = {}
+        out, dist = {}, {}
         for n, f in calls.items():
             reps_n = reps if n in ("gate_up_swiglu", "down") else 4 * reps
             out[n] = time_launches(torch, stream, f, reps_n, warm=2)
-        return out
+            dist[n] = launch_stats(torch, stream, f, reps_n, warm=0)
+        return out, dist
 
-    us = kernel_times(fp8.ACC_EXACT, 10)
+    us, us_dist = kernel_times(fp8.ACC_EXACT, 10)
     kernels = {
         "observe": {"us": us["observe"], "bytes": 2.0 * M * H,
                     "GB/s": 2.0 * M * H / us["observe"] / 1e3},
@@ -317,6 +335,8 @@ def main():
                  "TFLOP/s": tflops(down_flops, us["down"]),
                  "frac_fp8_peak": tflops(down_flops, us["down"]) / FP8_PEAK_TFLOPS},
     }
+    for n, d in us_dist.items():   # per-launch spread beside the back-to-back average
+        kernels[n].update(d)
     fused = tflops(fused_flops, us["gate_up_swiglu"])
     roofline = {
         "kernel": f"gate/up GEMMs + SwiGLU-FP8 epilogue, exact engine (F16 MFMA on exactly "
@@ -339,7 +359,7 @@ def main():
 
     # the native FP8 MFMA engine, same workload (context only)
     ms8 = timed_steps(fp8.ACC_FP8_MFMA, max(args.steps // 2, 5), 3)
-    us8 = kernel_times(fp8.ACC_FP8_MFMA, 5)
+    us8, _ = kernel_times(fp8.ACC_FP8_MFMA, 5)
     f8 = tflops(fused_flops, us8["gate_up_swiglu"])
     fp8_engine = {
         "meets_tolerance": False, "note": FP8_ENGINE_NOTE,
