@@ -123,3 +123,20 @@ def test_moving_average_clips_below_max_on_spiky_calls():
     from oracle.linear import quant_static
     q = quant_static(x, s_ma)
     assert np.count_nonzero((q & 0x7F) == 0x7E) > 0
+
+
+def test_observer_constants_are_the_printed_ones():
+    # the averaging constant and the calibration length the model card prints
+    # (tests/golden, cited there) are the oracle's defaults, the library's
+    # calibration constant and the seeded calibration recipe's length
+    import inspect
+    import json
+    import os
+    from mlp_fp8_quant_amd import calibration
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "pages_printed_values.json")))["observer"]
+    c = g["averaging_constant"]
+    for f in (observe, calibrate):
+        assert inspect.signature(f).parameters["c"].default == c
+    assert float(calibration.MA_CONSTANT) == c
+    assert workloads.CALIB_CALLS == g["calibration_calls"]
