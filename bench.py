@@ -536,8 +536,10 @@ def fused_topology(fp8, torch, dev, stream, workloads):
     re-quantized onto max(s), one [M, 2I] GEMM, one-input SwiGLU); and the two
     split GEMMs written into column slices of one [M, 2I] buffer (row stride
     2I) + one-input SwiGLU.  Split Q/K/V [3072, 4096] x 3 * [4096, 4096]
-    against one [3072, 12288] GEMM.  Also the share of codes the
-    re-quantization changed (gate and up)."""
+    against one [3072, 12288] GEMM, and what a downstream per-row consumer of
+    q and k (an RMS norm) costs on the split path's contiguous outputs and on
+    the fused GEMM's column slices (row stride 3 * 4096).  Also the share of
+    codes the re-quantization changed (gate and up)."""
     def timed(f, reps=20):
         return time_launches(torch, stream, lambda r: f(), reps, warm=2)
 
@@ -589,6 +591,16 @@ def fused_topology(fp8, torch, dev, stream, workloads):
                                                             outs=ys, workspace=wsq))
     out["qkv_fp8_composite_TFLOP/s"] = tflops(3 * 2.0 * Mq * Hq * Hq, out["qkv_fp8_composite_us"])
     out["qkv_quantize_us"] = timed(lambda: fp8.fp8_quant_static(xq, sc, out=wsq[:Mq * Hq].view(Mq, Hq)))
+    # the consumer side, timed last (its allocations perturbed the GEMM
+    # timings when it ran before them): the fused GEMM hands downstream code
+    # column slices that keep the fused row stride, split projections are
+    # contiguous.  A per-row RMS norm of q and k (torch's rms_norm, standing
+    # in for the downstream QK norm; not a step of this path) on both
+    if hasattr(torch.nn.functional, "rms_norm"):
+        rms, nw = torch.nn.functional.rms_norm, torch.ones(Hq, dtype=torch.bfloat16, device=dev)
+        qs, ks = ycat[:, :Hq], ycat[:, Hq:2 * Hq]
+        out["consumer_qk_rmsnorm_contiguous_us"] = timed(lambda: (rms(ys[0], (Hq,), nw), rms(ys[1], (Hq,), nw)))
+        out["consumer_qk_rmsnorm_strided_us"] = timed(lambda: (rms(qs, (Hq,), nw), rms(ks, (Hq,), nw)))
     del qa, ws, ys, wcat, ycat, xq, wsq
     torch.cuda.empty_cache()
     return out
