@@ -766,16 +766,27 @@ def elementwise_large(fp8, torch, dev, stream):
     return out
 
 
+def code_digest(path):
+    """sha256[:16] of a HIP source's code: its // comments and all white
+    space left out, so that a comment edit keeps a counter record valid and
+    any change to the code invalidates it."""
+    import hashlib
+    import re
+    words = []
+    for line in open(path, encoding="utf-8"):
+        words.extend(re.sub(r"//.*", "", line).split())
+    return hashlib.sha256(" ".join(words).encode()).hexdigest()[:16]
+
+
 def recorded_traffic(key, source):
     """HBM-side bytes per launch of a kernel, as recorded from rocprofv3
     FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy of known size) in
     profiles/traffic.md, or None when that record is missing or was taken
     from a different version of the kernel's source file."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.md")
     src = os.path.join(ROOT, "mlp_fp8_quant_amd", "csrc", source)
     try:
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        digest = code_digest(src)
         for line in open(path):
             cells = [c.strip() for c in line.strip().strip("|").split("|")]
             if len(cells) >= 5 and cells[0] == key and cells[4] == digest:

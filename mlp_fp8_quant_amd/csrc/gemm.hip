@@ -26,9 +26,10 @@
 //  * a workgroup computes a BM x BN tile with WM x WN waves, each wave a
 //    (BM/WM) x (BN/WN) sub-tile of 32x32 MFMA blocks;
 //  * operands are K-contiguous ([M,K] and [N,K]); a stage holds 128 K of the
-//    tile's A and B rows (128 LDS bytes per row), two stages live in LDS and
-//    the buffer unit copies them from memory straight into LDS, one stage
-//    ahead of the MFMAs, one barrier per stage (details below);
+//    tile's A and B rows (128 LDS bytes per row), two stages live in LDS
+//    (three or four in the deep-prefetch variants) and the buffer unit copies
+//    them from memory straight into LDS ahead of the MFMAs, one barrier per
+//    stage (details below);
 //  * the 16-byte chunk c of LDS row r lives at chunk c ^ ((r >> 1) & 7): the
 //    LDS serves a 128-bit access 16 lanes at a time across 64 four-byte
 //    banks (256 bytes = two rows), and 16 consecutive rows of one logical
