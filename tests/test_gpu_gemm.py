@@ -291,3 +291,47 @@ def test_many_tiles_ragged_edges_and_k_tail(accum, K, M, N):
         check_gemm_bf16(yb, y32, S, A, alpha)
     else:
         check_gemm_fp8_engine(y32[:16], S[:16], A[:16], alpha, fp8_mfma_group_bound(qa[rows[:16]], qb))
+
+
+@pytest.mark.parametrize("accum", ENGINES)
+@pytest.mark.parametrize("M,N,K", [(37, 45, 272), (513, 3000, 384), (2600, 5000, 512)])
+def test_nan_codes_propagate(accum, M, N, K):
+    # R-19: a NaN code (0x7F or 0xFF) in A makes its whole output row NaN, one
+    # in B its whole output column (NaN times anything, zero included, is
+    # NaN); every other output is the oracle's; BF16 outputs there are NaN and
+    # FP8 outputs the NaN code 0x7F.  The shapes take the 128x64 kernel with
+    # the K split, without it, and 256x256 tiles.
+    dev = device()
+    print(f"case accum={accum} M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M + N + K + accum)
+    qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
+    nan_rows, nan_cols = [M // 7, M - 1], [N // 3]
+    qa[nan_rows[0], K // 2] = 0x7F
+    qa[nan_rows[1], 3] = 0xFF
+    qb[nan_cols[0], K - 1] = 0x7F
+    sx, sw = np.float32(0.0213), np.float32(1.7e-4)
+    sy = np.float32(0.05)
+    out = _run(qa, qb, sx, sw, dev, kinds=(fp8.OUT_F32, fp8.OUT_BF16, fp8.OUT_FP8), sy=sy,
+               accum=accum)
+    y32, yb, y8 = host_f32(out[fp8.OUT_F32]), host_bits(out[fp8.OUT_BF16]), host_u8(out[fp8.OUT_FP8])
+    mask = np.zeros((M, N), bool)
+    mask[nan_rows, :] = True
+    mask[:, nan_cols] = True
+    assert np.array_equal(np.isnan(y32), mask)
+    assert np.array_equal((yb & 0x7FFF) > 0x7F80, mask)      # BF16 NaN patterns exactly there
+    assert np.all(y8[mask] == 0x7F)
+    # elsewhere: the oracle (checked on the NaN rows' neighbours and a sample)
+    rows = np.unique(np.concatenate([np.clip(np.array(nan_rows) + 1, 0, M - 2),
+                                     rng.choice(M, min(M, 48), replace=False)]))
+    rows = rows[~np.isin(rows, nan_rows)]
+    cols = np.setdiff1d(np.arange(N), nan_cols)
+    S, A = olin.gemm_exact(qa[rows], qb[cols])
+    alpha = olin.epilogue_alpha(sx, sw)
+    sub = y32[np.ix_(rows, cols)]
+    if accum == fp8.ACC_EXACT:
+        check_gemm_f32(sub, S, A, alpha)
+    else:   # the group bound is costly: 16 rows x 2048 columns
+        r, c = slice(0, 16), slice(0, 2048)
+        check_gemm_fp8_engine(sub[r, c], S[r, c], A[r, c], alpha,
+                              fp8_mfma_group_bound(qa[rows[r]], qb[cols[c]]))
+    assert np.array_equal(yb[np.ix_(rows, cols)], f32_to_bf16(sub))
