@@ -153,6 +153,28 @@ def test_fp8_output_is_the_encoded_f32_output(accum, M, N, K):
     assert np.array_equal(host_u8(out[fp8.OUT_FP8]), want)
 
 
+@pytest.mark.parametrize("accum", ENGINES)
+@pytest.mark.parametrize("sy", [1e-3, 64.0])
+def test_fp8_output_saturates_and_underflows_as_encoded(accum, sy):
+    # the FP8 epilogue at an output scale that saturates most outputs to
+    # +-448 (0x7E / 0xFE) and at one that takes most into the subnormal range
+    # or to signed zero: still bit for bit the encoding of the FP32 output
+    dev = device()
+    M, N, K = 257, 385, 1040
+    rng = np.random.default_rng(77 + accum)
+    qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
+    sx, sw, sy = np.float32(0.0213), np.float32(1.7e-4), np.float32(sy)
+    out = _run(qa, qb, sx, sw, dev, kinds=(fp8.OUT_F32, fp8.OUT_FP8), sy=sy, accum=accum)
+    y32 = host_f32(out[fp8.OUT_F32])
+    got = host_u8(out[fp8.OUT_FP8])
+    assert np.array_equal(got, e4m3_encode((y32 / sy).astype(np.float32)))
+    mag = got & 0x7F
+    if sy < 1:
+        assert np.count_nonzero(mag == 0x7E) > M * N // 2      # saturated
+    else:
+        assert np.count_nonzero(mag < 0x08) > M * N // 4       # subnormal codes or zero
+
+
 def _linear_case(x_bits, w_bits, dev, rows=None, accum=fp8.ACC_EXACT, key=None):
     """Quantize x and w as the method does and compare one projection;
     `key` names the figures reported (the outputs that needed R-13's second
