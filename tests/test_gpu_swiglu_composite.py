@@ -391,3 +391,32 @@ def test_degenerate_qkv_shapes(accum):
     yq, yk, yv = fp8.qkv_fp8(x, ds[0], e(ns[0], 64).zero_(), ds[1], e(ns[1], 64).zero_(), ds[2],
                              e(ns[2], 64).zero_(), ds[3], accum=accum)
     assert (yq.shape, yk.shape, yv.shape) == ((0, 64), (0, 32), (0, 48))
+
+
+@pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+@pytest.mark.parametrize("sh", [1e-5, 1e3])
+def test_fused_epilogue_saturates_and_underflows_as_parts(accum, sh):
+    # the fused kernel's SwiGLU epilogue at a down-input scale that saturates
+    # most codes and at one that takes most to subnormal codes or zero:
+    # bitwise the separate gate/up GEMMs + silu_mul_2in_fp8 (I >= H)
+    dev = device()
+    M, I, H = 300, 1024, 512
+    rng = np.random.default_rng(51 + accum)
+    x = workloads.activations(rng, M, H)
+    wg = workloads.weights(rng, I, H, 0.02)
+    wu = workloads.weights(rng, I, H, 0.02)
+    sx = olin.scale_from_amax(olin.amax_f32(x))
+    qx = to_dev_u8(olin.quant_static(x, sx), dev)
+    (qg, sg), (qu, su) = olin.rtn_weight(wg), olin.rtn_weight(wu)
+    dg, du = to_dev_u8(qg, dev), to_dev_u8(qu, dev)
+    dsx, dsg, dsu, dsh = (scalar(v, dev) for v in (sx, sg, su, sh))
+    qh = fp8.fp8_gate_up_swiglu(qx, dg, dsx, dsg, du, dsu, dsh, accum=accum)
+    G = fp8.fp8_linear(qx, dg, dsx, dsg, accum=accum)
+    U = fp8.fp8_linear(qx, du, dsx, dsu, accum=accum)
+    parts = fp8.silu_mul_2in_fp8(G, U, dsh)
+    assert torch.equal(qh, parts)
+    mag = host_u8(qh) & 0x7F
+    if sh < 1:
+        assert np.count_nonzero(mag == 0x7E) > mag.size // 2
+    else:
+        assert np.count_nonzero(mag < 0x08) > mag.size // 2
