@@ -177,3 +177,43 @@ def test_rowwise_refusals():
         fp8.fp8_linear_rowwise(q, q, s4[:3], s4)
     with pytest.raises(fp8.Fp8motError):
         fp8.fp8_quant_per_row(torch.zeros((4, 24), dtype=torch.bfloat16, device=dev))
+
+
+@pytest.mark.parametrize("engine", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
+def test_linear_rowwise_special_scales(engine):
+    # per-row scales NaN (a NaN row), 0 (a zero row) and +Inf (an Inf row),
+    # per-channel scales 0 and NaN: alpha[m, n] = fp32(s_x[m] * s_w[n]) and
+    # y = fp32(acc * alpha) give NaN, signed infinities and zeros exactly
+    # where the oracle's epilogue does (R-24); the rest meets the GEMM bar
+    dev = device()
+    M, N, K = 40, 48, 272
+    rng = np.random.default_rng(60 + engine)
+    qx = rng.integers(0, 256, (M, K), dtype=np.int64).astype(np.uint8)
+    qw = rng.integers(0, 256, (N, K), dtype=np.int64).astype(np.uint8)
+    qx[(qx & 0x7F) == 0x7F] = 0x7E
+    qw[(qw & 0x7F) == 0x7F] = 0x7E
+    sx = rng.uniform(0.01, 0.1, M).astype(np.float32)
+    sw = rng.uniform(1e-4, 1e-3, N).astype(np.float32)
+    sx[3], sx[5], sx[8] = np.nan, 0.0, np.inf
+    sw[7], sw[11] = 0.0, np.nan
+    d = lambda a: torch.from_numpy(a).to(dev)   # noqa: E731
+    y32 = host_f32(fp8.fp8_linear_rowwise(d(qx), d(qw), d(sx), d(sw), out_kind=fp8.OUT_F32, accum=engine))
+    yb = host_bits(fp8.fp8_linear_rowwise(d(qx), d(qw), d(sx), d(sw), accum=engine))
+    S, A = gemm_exact(qx, qw)
+    with np.errstate(invalid="ignore", over="ignore"):
+        want = epilogue_rowwise_f32(S, sx, sw)
+    assert np.array_equal(np.isnan(y32), np.isnan(want))
+    inf = np.isinf(want)
+    assert inf.any() and np.array_equal(y32[inf], want[inf])
+    zero = want == 0
+    assert zero.any() and np.all(y32[zero] == 0)
+    fin = np.isfinite(want) & ~zero
+    alpha = epilogue_rowwise_alpha(sx, sw).astype(np.float64)
+    err = np.abs(y32[fin].astype(np.float64) - alpha[fin] * S[fin])
+    bound = 1e-5 * A
+    if engine != fp8.ACC_EXACT:
+        bound = bound + fp8_mfma_group_bound(qx, qw)
+    assert np.all(err <= alpha[fin] * bound[fin])
+    bits_nan = (yb & 0x7FFF) > 0x7F80
+    assert np.array_equal(bits_nan, np.isnan(want))
+    assert np.array_equal(yb[~bits_nan], f32_to_bf16(y32)[~bits_nan])
