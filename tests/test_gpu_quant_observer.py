@@ -133,6 +133,39 @@ def test_observer_nan_propagates():
 
 
 @pytest.mark.parametrize("mode", [fp8.OBS_MAX, fp8.OBS_MOVING_AVG])
+def test_observer_infinities_and_negative_nan(mode):
+    # a call holding -Inf has amax +Inf, which both observers fold to +Inf
+    # (m + c * (Inf - m) = Inf); after it a finite call keeps the max at Inf
+    # but turns the moving average into NaN (Inf + c * (a - Inf) is
+    # Inf - Inf); a NaN pattern with the sign bit set (0xFFC1) counts as NaN.
+    # Max: 3, Inf, Inf, NaN; moving average: 3, Inf, NaN, NaN -- each state
+    # bit for bit the oracle's, the final scale NaN
+    dev = device()
+    st = fp8.new_observer_state(dev)
+    ost = oobs.ObserverState()
+    calls = []
+    base = workloads.to_bf16_bits(np.linspace(-3, 2, 5000).astype(np.float32))
+    calls.append(base.copy())
+    inf_call = base.copy()
+    inf_call[77] = 0xFF80                     # -Inf
+    calls.append(inf_call)
+    calls.append(base.copy())
+    nan_call = base.copy()
+    nan_call[4000] = 0xFFC1                   # a NaN with the sign bit set
+    calls.append(nan_call)
+    for c in calls:
+        fp8.fp8_observe(to_dev_bf16(c, dev), st, mode, 0.01)
+        with np.errstate(invalid="ignore"):     # Inf - Inf in the oracle's update
+            oobs.observe(ost, oobs.call_amax(c), mode, 0.01)
+        got = _state_host(st)[0]
+        want = np.float32(ost.m)
+        assert (np.isnan(got) and np.isnan(want)) or got.view(np.uint32) == want.view(np.uint32)
+    assert oobs.call_amax(inf_call) == np.inf and np.isnan(oobs.call_amax(nan_call))
+    s = host_f32(fp8.fp8_scale_from_state(st))[0]
+    assert np.isnan(s) and np.isnan(olin.scale_from_amax(ost.m))
+
+
+@pytest.mark.parametrize("mode", [fp8.OBS_MAX, fp8.OBS_MOVING_AVG])
 def test_two_tower_calibration_und_full(mode):
     # 256 calibration calls of the und tower at full size ([512, 4096] group
     # inputs, [512, 12288] down input), both observers, bit-exact
