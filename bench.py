@@ -217,7 +217,7 @@ def parse():
     p.add_argument("--no-blocks", action="store_true",
                    help="only the headline step and its kernels (for profiling runs)")
     p.add_argument("--blocks", default="gen_mlp,elementwise_large,per_row_fp8,fused_topology,"
-                                       "two_tower_layer,library_references",
+                                       "two_tower_layer,library_references,single_linear",
                    help="comma-separated extra blocks to run")
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="also run one plain device copy of this many MiB (a "
@@ -393,6 +393,8 @@ def main():
         blocks["fused_topology"] = fused_topology(fp8, torch, dev, stream, workloads)
     if "two_tower_layer" in want:
         blocks["two_tower_layer"] = two_tower_layer(fp8, torch, dev, stream)
+    if "single_linear" in want:
+        blocks["single_linear"] = single_linear(fp8, torch, dev, stream, workloads)
 
     if args.copy_calib_mb > 0:
         n = args.copy_calib_mb << 20
@@ -603,6 +605,77 @@ def fused_topology(fp8, torch, dev, stream, workloads):
         out["consumer_qk_rmsnorm_strided_us"] = timed(lambda: (rms(qs, (Hq,), nw), rms(ks, (Hq,), nw)))
     del qa, ws, ys, wcat, ycat, xq, wsq
     torch.cuda.empty_cache()
+    return out
+
+
+def single_linear(fp8, torch, dev, stream, workloads):
+    """The single-Linear workload (X [64, 512] with outliers, W [512, 512],
+    per-tensor static scales): quantize + one GEMM, 33.6 MFLOP over ~0.4 MB,
+    a latency-bound call.  Back-to-back eager calls (the binding's host cost
+    included) and each kernel alone; HIP graphs holding one call, 50 calls,
+    50 quantizations and 50 GEMMs, whose replays give the GPU time per call
+    with one graph launch spread over 100 kernels (each graph's output
+    checked against the eager one, synchronizing between replays)."""
+    wl = workloads.single_linear()
+    x = dev_bf16(torch, wl.x, dev)
+    qw, sw = fp8.rtn_weight(dev_bf16(torch, wl.weights["w"], dev))
+    st = fp8.new_observer_state(dev)
+    fp8.fp8_observe(x, st, fp8.OBS_MAX)
+    sx = fp8.fp8_scale_from_state(st)
+    M, K = x.shape
+    N = qw.shape[0]
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        fp8.fp8_quant_static(x, sx, out=qx)
+        fp8.fp8_linear(qx, qw, sx, sw, out=y)
+
+    flops = 2.0 * M * N * K
+    out = {"workload": wl.name, "flops": flops}
+    out["eager_call_us"] = time_launches(torch, stream, lambda r: call(), 500, warm=20)
+    out["quant_us"] = time_launches(torch, stream, lambda r: fp8.fp8_quant_static(x, sx, out=qx), 500, warm=20)
+    out["gemm_us"] = time_launches(torch, stream, lambda r: fp8.fp8_linear(qx, qw, sx, sw, out=y), 500, warm=20)
+    call()
+    torch.cuda.synchronize()
+    ref = y.clone()
+
+    def graph_of(fn, n):
+        side = torch.cuda.Stream(device=dev)   # warm-up on a side stream before capture
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        return g
+
+    quant = lambda: fp8.fp8_quant_static(x, sx, out=qx)        # noqa: E731
+    gemm = lambda: fp8.fp8_linear(qx, qw, sx, sw, out=y)        # noqa: E731
+    graphs = {"one_call": graph_of(call, 1), "calls": graph_of(call, 50),
+              "quant": graph_of(quant, 50), "gemm": graph_of(gemm, 50)}
+    for name in ("one_call", "calls", "gemm"):
+        for _ in range(3):
+            y.zero_()
+            torch.cuda.synchronize()
+            graphs[name].replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"{name} graph differs"
+    t = {k: time_launches(torch, stream, lambda r, g=g: g.replay(), 100, warm=5) for k, g in graphs.items()}
+    out["graph_one_call_us"] = t["one_call"]
+    # GPU time: 50 calls (100 launches) captured in one graph, per call
+    out["gpu_call_us"] = t["calls"] / 50
+    out["gpu_quant_us"] = t["quant"] / 50
+    out["gpu_gemm_us"] = t["gemm"] / 50
+    out["gpu_TFLOP/s"] = tflops(flops, out["gpu_call_us"])
+    out["note"] = ("latency-bound: eager calls are bound by the host (two library calls); a graph "
+                   "holding one call costs more to launch than the two eager launches it replaces; "
+                   "gpu_* are per call from 50 calls captured in one graph")
+    del graphs
     return out
 
 
