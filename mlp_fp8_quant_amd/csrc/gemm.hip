@@ -887,13 +887,16 @@ int forced_env(const char* name) {
 // ~0.7 tiles per CU; below that 256x128 (8 waves), then 128x128 and 128x64
 // (4 waves; 512x4096x4096: 33.9 -> 25.8 us, 512x4096x12288: 72.7 -> 55.6 us
 // with 128x64) keep the CUs busy.  Where 256x256 tiles are used, 192x256
-// tiles (8 waves of 96x64) replace them when they fill the rounds of one
-// workgroup per CU better: both run one workgroup per CU, and a 192x256 tile
-// takes ~0.92 of a 256x256 tile's time, so the rounds are compared at that
-// weight (split Q/K/V, 3072 x 3*4096 x 4096: 576 tiles of 256x256 are 2.25
-// per CU, 768 of 192x256 exactly 3; 298.5 -> 273.2 us, and 185.6 -> 163.9 us
-// for 1536 rows).  FP8MOT_GEMM_CFG=<1|5|3|6|7> forces one configuration
-// (tuning; 6 is 128x64, 7 is 192x256).
+// tiles (8 waves of 96x64, one workgroup per CU as well) replace them when
+// they need no more rounds of one workgroup per CU: per FLOP they run 3-4%
+// slower (whole rounds on both, 12288x4096x4096: 299 against 309-311 us), so
+// they pay only where they fill a round that 256x256 tiles leave partly empty
+// (split Q/K/V, 3072 x 3*4096 x 4096: 576 tiles of 256x256 are 2.25 per CU,
+// 768 of 192x256 exactly 3; 274 -> 232 us, and 185.6 -> 163.9 us for 1536
+// rows).  Needing one round more, they came out within -3% .. +1.5%
+// (4608x12288x4096, 6144x12288x4096: a partial last round costs less than a
+// full one), so 256x256 stays there.  FP8MOT_GEMM_CFG=<1|5|3|6|7> forces one
+// configuration (tuning; 6 is 128x64, 7 is 192x256).
 int pick_cfg(int64_t tiles_256x256, int64_t tiles_192x256, int64_t tiles_256x128,
              int64_t tiles_128x128, int num_cus) {
   static const int forced = forced_env("FP8MOT_GEMM_CFG");
@@ -902,7 +905,7 @@ int pick_cfg(int64_t tiles_256x256, int64_t tiles_192x256, int64_t tiles_256x128
   if (tiles_256x256 >= want) {
     const int64_t r256 = (tiles_256x256 + num_cus - 1) / num_cus;
     const int64_t r192 = (tiles_192x256 + num_cus - 1) / num_cus;
-    return r192 * 92 < r256 * 100 ? 7 : 1;
+    return r192 <= r256 ? 7 : 1;
   }
   if (tiles_256x128 >= want) return 5;
   return tiles_128x128 >= want ? 3 : 6;
