@@ -1,6 +1,6 @@
 """GPU check of the composites' tile scheduling on assorted ragged shapes: the
-fused gate/up + SwiGLU kernel (persistent, several tiles per workgroup from
-~0.7 tile per CU upwards, ragged M and I, K = H a multiple of 128 or not)
+fused gate/up + SwiGLU kernel (from a single tile to several per workgroup
+in its persistent loop, ragged M and I, K = H a multiple of 128 or not)
 bitwise equal to two fp8_linear calls + silu_mul_2in_fp8 when I >= H; and
 the grouped split-Q/K/V launch (unequal member widths, an empty member)
 bitwise equal to three fp8_linear calls on the one quantized activation."""
@@ -32,7 +32,7 @@ def _codes(rng, shape):
 
 @pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
 @pytest.mark.parametrize("M,I,H", FUSED)
-def test_fused_gate_up_random_shapes_equal_parts(accum, M, I, H):
+def test_fused_gate_up_shapes_equal_parts(accum, M, I, H):
     dev = device()
     print(f"fused M={M} I={I} H={H} accum={accum}", flush=True)
     rng = np.random.default_rng(M * 31 + I * 7 + H + accum)
@@ -46,7 +46,7 @@ def test_fused_gate_up_random_shapes_equal_parts(accum, M, I, H):
 
 @pytest.mark.parametrize("accum", [fp8.ACC_EXACT, fp8.ACC_FP8_MFMA])
 @pytest.mark.parametrize("M,H,Nq,Nk,Nv", QKV)
-def test_qkv_grouped_random_shapes_equal_separate(accum, M, H, Nq, Nk, Nv):
+def test_qkv_grouped_shapes_equal_separate(accum, M, H, Nq, Nk, Nv):
     dev = device()
     print(f"qkv M={M} H={H} N={Nq},{Nk},{Nv} accum={accum}", flush=True)
     rng = np.random.default_rng(M + H + Nq + 3 * Nk + 7 * Nv + accum)
