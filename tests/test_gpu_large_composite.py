@@ -25,7 +25,8 @@ from oracle import linear as olin
 from oracle.swiglu import silu_mul_f64, silu_mul_fp8
 
 from gpu_util import (check_fp8_tolerance, check_gemm_bf16, check_gemm_f32, device,
-                      host_bits, host_f32, host_u8, scalar, to_dev_bf16, to_dev_u8)
+                      host_bits, host_f32, host_u8, oracle_rtn_threaded, scalar, to_dev_bf16,
+                      to_dev_u8)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,3 +93,47 @@ def test_large_down_shape_random_codes_sampled():
     f = host_f32(y32[r][:, c])
     check_gemm_f32(f, S, A, alpha)
     check_gemm_bf16(host_bits(yb[r][:, c]), f, S, A, alpha)
+
+
+def test_large_gated_mlp_sampled_rows_through_the_whole_chain():
+    # 16 token rows of the large gated MLP through every stage at full width,
+    # each oracle stage consuming the GPU's previous-stage output: all codes
+    # of the three RTN weights; qX of the rows; all 25600 SwiGLU codes of each
+    # row against the oracle's chain (exact sums, BF16 epilogue, SwiGLU,
+    # encode) within the SwiGLU bar; the down projection of the GPU's qH rows
+    # against the exact sum (FP32 output of the same kernel within
+    # 1e-5 * sum|terms|, the composite's BF16 output per R-13)
+    dev = device()
+    wl = workloads.gated_mlp(0, M, H, I, std=0.015)
+    rows = np.sort(np.random.default_rng(14).choice(M, 16, replace=False))
+    r = torch.from_numpy(rows).to(dev)
+    dq, ds, oq, os_ = {}, {}, {}, {}
+    for k, w in wl.weights.items():
+        print(f"RTN {k} {w.shape}", flush=True)
+        dq[k], ds[k] = fp8.rtn_weight(to_dev_bf16(w, dev))
+        oq[k], os_[k] = oracle_rtn_threaded(w)
+        assert ds[k].item() == float(os_[k]), k
+        assert np.array_equal(host_u8(dq[k]), oq[k]), k
+    sx = olin.scale_from_amax(olin.amax_f32(wl.x))
+    qx_rows = olin.quant_static(wl.x[rows], sx)
+    Sg, _ = olin.gemm_exact(qx_rows, oq["gate"])
+    Su, _ = olin.gemm_exact(qx_rows, oq["up"])
+    G = olin.epilogue_bf16(Sg, sx, os_["gate"])
+    U = olin.epilogue_bf16(Su, sx, os_["up"])
+    sh = olin.scale_from_amax(np.float32(np.max(np.abs(silu_mul_f64(G, U)))))
+    dx = to_dev_bf16(wl.x, dev)
+    dsx, dsh = scalar(sx, dev), scalar(sh, dev)
+    y = fp8.gated_mlp_fp8(dx, dsx, dq["gate"], ds["gate"], dq["up"], ds["up"], dsh,
+                          dq["down"], ds["down"])
+    qx = fp8.fp8_quant_static(dx, dsx)
+    qh = fp8.fp8_gate_up_swiglu(qx, dq["gate"], dsx, ds["gate"], dq["up"], ds["up"], dsh)
+    y32 = fp8.fp8_linear(qh, dq["down"], dsh, ds["down"], fp8.OUT_F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(qx[r]), qx_rows)
+    qh_rows = host_u8(qh[r])
+    check_fp8_tolerance(qh_rows.ravel(), silu_mul_fp8(G, U, sh))
+    S, A = olin.gemm_exact(qh_rows, oq["down"])
+    alpha = olin.epilogue_alpha(sh, os_["down"])
+    f = host_f32(y32[r])
+    check_gemm_f32(f, S, A, alpha)
+    check_gemm_bf16(host_bits(y[r]), f, S, A, alpha)
