@@ -318,7 +318,9 @@ size_t gated_mlp_fp8_workspace(int64_t M, int64_t H, int64_t I);
  * x: [M, H]; wg, wu: [I, H]; wd: [H, I];
  * y: [M, H].  H and I multiples of 16.  ws: device workspace of at least
  * gated_mlp_fp8_workspace(M, H, I) bytes, 256-byte aligned.  `accum`
- * selects the GEMM engine (fp8mot_acc) of all three GEMMs. */
+ * selects the GEMM engine (fp8mot_acc) of all three GEMMs.  I == 0 (empty
+ * weights, whose pointers may be NULL) writes y = 0, the down projection of
+ * an empty sum; M == 0 or H == 0 writes nothing. */
 int gated_mlp_fp8(const uint16_t* x, int64_t M, int64_t H, int64_t I,
                   const float* d_sx, const uint8_t* wg, const float* d_sg,
                   const uint8_t* wu, const float* d_su, const float* d_sh,
