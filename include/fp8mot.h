@@ -371,6 +371,8 @@ size_t qkv_fp8_workspace(int64_t M, int64_t H);
  * The three GEMMs run as one grouped launch, or as three launches when
  * fp8_linear would split K for one of them; either way bitwise what three
  * fp8_linear calls give.  A member with N == 0 is skipped and its pointers may be NULL.
+ * H == 0 quantizes nothing (x, the weights and ws may be NULL) and writes each
+ * projection's epilogue of an empty sum, zero; M == 0 writes nothing.
  * Cross-attention, where k/v read a different tensor than q, must not use
  * this call: quantize each input separately and use fp8_linear.  `accum`
  * selects the GEMM engine (fp8mot_acc). */
