@@ -921,14 +921,18 @@ int pick_cfg(int64_t tiles_256x256, int64_t tiles_192x256, int64_t tiles_256x128
 template <int BM, int BN, int WM, int WN, int ENGINE>
 hipError_t launch_cfg(GemmArgs a, int out_kind, int num_cus, hipStream_t stream, bool split) {
   set_tiles<BM, BN>(a);
-  if constexpr (BM == 128) {
+  // (the FP8 engine never splits 128x64 tiles, and only the FP8 engine takes
+  // deep prefetch without a split: the other combinations are not built)
+  if constexpr (BM == 128 && !(ENGINE == 1 && BN == 64)) {
     // 128x64 tiles leave room for three stages per K group (measured on the
     // und tower's 512x4096x12288 down projection, whose copies the two-stage
     // loop waits on)
     if (split) return launch_tiled<BM, BN, WM, WN, ENGINE, BN == 64, 2>(a, out_kind, num_cus, stream);
   }
-  const bool deep = ENGINE == 1 && (BM + BN > 256 || (int64_t)a.tiles_m * a.tiles_n <= num_cus);
-  if (deep) return launch_tiled<BM, BN, WM, WN, ENGINE, true, 1>(a, out_kind, num_cus, stream);
+  if constexpr (ENGINE == 1) {
+    if (BM + BN > 256 || (int64_t)a.tiles_m * a.tiles_n <= num_cus)
+      return launch_tiled<BM, BN, WM, WN, ENGINE, true, 1>(a, out_kind, num_cus, stream);
+  }
   return launch_tiled<BM, BN, WM, WN, ENGINE, false, 1>(a, out_kind, num_cus, stream);
 }
 
