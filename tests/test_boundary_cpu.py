@@ -36,6 +36,25 @@ def test_header_declares_the_hot_path_calls():
         assert n in names
 
 
+def test_header_is_valid_c(tmp_path):
+    # the ABI is C: the header compiles as C11 with every warning an error
+    # (the ROCm headers it includes as system headers), and every declared
+    # function is referenced by name from C
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.fail("gcc is required to check the header as C")
+    src = tmp_path / "uses_header.c"
+    refs = "\n".join(f"  (void)&{n};" for n in declared_functions())
+    src.write_text('#include "fp8mot.h"\nint main(void) {\n' + refs + "\n  return 0;\n}\n")
+    r = subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-D__HIP_PLATFORM_AMD__", "-isystem", "/opt/rocm/include",
+                        "-I", os.path.dirname(HEADER), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     for n in declared_functions():
