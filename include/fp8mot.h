@@ -170,6 +170,32 @@ int fp8mot_mfma_ceiling(const uint8_t* a, int64_t na, const uint8_t* b, int64_t 
                         int64_t iters, int accum, float* sink, double* flops,
                         hipStream_t stream);
 
+/* Conversion of fp8mot_convert_f32. */
+typedef enum {
+  FP8MOT_CONV_E4M3_PACKED = 0, /* packed gfx950 conversion after a NaN-propagating clamp to
+                                  +-448, NaN bytes set to 0x7F: the quantize and SwiGLU
+                                  kernels' bodies and the GEMMs' FP8 output */
+  FP8MOT_CONV_E4M3_INT = 1,    /* integer round-to-nearest-even on the bit pattern: the
+                                  elementwise kernels' tails */
+  FP8MOT_CONV_BF16 = 2         /* packed gfx950 BF16 conversion: the GEMM epilogues */
+} fp8mot_conv;
+
+/* Verification aid, not a step of the path: the FP32 -> E4M3 and FP32 ->
+ * BF16 conversions of the path's kernels, applied to any FP32 input, so that
+ * they can be checked on every FP32 bit pattern against the encoding rules
+ * ([MC] "Scheme": E4M3 with round to nearest even; the library saturates to
+ * +-448, maps NaN to 0x7F and keeps the sign of zero; BF16 round to nearest
+ * even, NaN stays NaN).
+ *   kind FP8MOT_CONV_E4M3_PACKED or FP8MOT_CONV_E4M3_INT:
+ *     out: uint8_t [n], out[i] = the E4M3 code of x[i];
+ *   kind FP8MOT_CONV_BF16:
+ *     out: uint16_t [n], out[i] = the BF16 bits of x[i].
+ * x: float [n], 16-byte aligned; out 16-byte aligned.  n must be a multiple
+ * of 4 (the kernels convert four values at a time); n == 0 is a no-op.
+ * Refusals: n < 0, n % 4 != 0, another kind, or (n > 0) a NULL pointer ->
+ * FP8MOT_ERR_INVALID_ARG; a misaligned pointer -> FP8MOT_ERR_MISALIGNED. */
+int fp8mot_convert_f32(const float* x, void* out, int64_t n, int kind, hipStream_t stream);
+
 /* ------------------------------------------------------------------ */
 /* Steps of the hot path                                               */
 /* ------------------------------------------------------------------ */

@@ -6,10 +6,11 @@ PyTorch binding with the same names.  The library is loaded on first use and
 its absence is an error -- there is no CPU path.
 """
 
-from .api import (ACC_EXACT, ACC_FP8_MFMA, OBS_MAX,  # noqa: F401
+from .api import (ACC_EXACT, ACC_FP8_MFMA, CONV_BF16, CONV_E4M3_INT,  # noqa: F401
+                  CONV_E4M3_PACKED, OBS_MAX,
                   OBS_MOVING_AVG, OUT_BF16, OUT_F32,
                   OUT_FP8, Fp8motError, debug_quant_launches,
-                  fp8_check_shared_scale, fp8_gate_up_swiglu, fp8_linear,
+                  convert_f32, fp8_check_shared_scale, fp8_gate_up_swiglu, fp8_linear,
                   fp8_linear_into, fp8_linear_rowwise, fp8_quant_per_row,
                   fp8_requantize_onto_max,
                   fp8_observe,

@@ -23,6 +23,7 @@ SIGNATURES = {
     "fp8mot_rw_ceiling": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_void_p]),
     "fp8mot_mfma_ceiling": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_i64, c_int, c_void_p,
                                    ctypes.POINTER(ctypes.c_double), c_void_p]),
+    "fp8mot_convert_f32": (c_int, [c_void_p, c_void_p, c_i64, c_int, c_void_p]),
     "fp8_quant_static": (c_int, [c_void_p, c_void_p, c_i64, c_void_p, c_void_p]),
     "fp8_linear": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64,
                            c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p]),

@@ -22,6 +22,7 @@ from ._lib import Fp8motError  # noqa: F401
 OUT_BF16, OUT_FP8, OUT_F32 = 0, 1, 2
 ACC_EXACT, ACC_FP8_MFMA = 0, 1
 OBS_MAX, OBS_MOVING_AVG = 0, 1
+CONV_E4M3_PACKED, CONV_E4M3_INT, CONV_BF16 = 0, 1, 2
 _OUT_DTYPE = {OUT_BF16: torch.bfloat16, OUT_FP8: torch.uint8, OUT_F32: torch.float32}
 
 
@@ -460,6 +461,23 @@ def mfma_ceiling(a, b, iters, sink, accum=ACC_EXACT):
     _lib.call("fp8mot_mfma_ceiling", _ptr(a), a.numel(), _ptr(b), b.numel(), int(iters),
               int(accum), _ptr(sink), ctypes.byref(flops), _stream(a))
     return flops.value
+
+
+def convert_f32(x, kind=CONV_E4M3_PACKED, out=None):
+    """Verification aid: the kernels' FP32 -> E4M3 (kind CONV_E4M3_PACKED or
+    CONV_E4M3_INT; uint8 codes) or FP32 -> BF16 (CONV_BF16; bfloat16 bits)
+    conversion of every element of the float32 GPU tensor x (numel a
+    multiple of 4).  Returns out (allocated when None)."""
+    _need(x, "x", torch.float32)
+    dtype = torch.bfloat16 if kind == CONV_BF16 else torch.uint8
+    if out is None:
+        out = torch.empty(x.shape, dtype=dtype, device=x.device)
+    else:
+        _need(out, "out", dtype, x.device)
+        if out.numel() != x.numel():
+            raise ValueError("out must have as many elements as x")
+    _lib.call("fp8mot_convert_f32", _ptr(x), _ptr(out), x.numel(), int(kind), _stream(x))
+    return out
 
 
 def debug_quant_launches():

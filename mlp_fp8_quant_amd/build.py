@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfp8mot.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["elementwise.hip", "gemm.hip", "mfma_ceiling.hip", "capi.hip"]
+SOURCES = ["elementwise.hip", "gemm.hip", "mfma_ceiling.hip", "verify.hip", "capi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

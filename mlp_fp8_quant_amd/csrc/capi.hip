@@ -157,6 +157,19 @@ int fp8mot_mfma_ceiling(const uint8_t* a, int64_t na, const uint8_t* b, int64_t 
   return hip_status(launch_mfma_ceiling(a, na, b, nb, iters, accum, sink, cus, stream));
 }
 
+int fp8mot_convert_f32(const float* x, void* out, int64_t n, int kind, hipStream_t stream) {
+  if (n < 0 || n % 4 != 0) return FP8MOT_ERR_INVALID_ARG;
+  if (kind != FP8MOT_CONV_E4M3_PACKED && kind != FP8MOT_CONV_E4M3_INT && kind != FP8MOT_CONV_BF16)
+    return FP8MOT_ERR_INVALID_ARG;
+  if (n == 0) return FP8MOT_OK;
+  if (x == nullptr || out == nullptr) return FP8MOT_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out)) return FP8MOT_ERR_MISALIGNED;
+  int cus = 0;
+  int st = current_device(&cus);
+  if (st != FP8MOT_OK) return st;
+  return hip_status(launch_convert_f32(x, out, n, kind, ew_blocks(cus), stream));
+}
+
 int fp8_quant_static(const uint16_t* x, uint8_t* q, int64_t n,
                      const float* d_scale, hipStream_t stream) {
   if (d_scale == nullptr) return FP8MOT_ERR_UNSUPPORTED;

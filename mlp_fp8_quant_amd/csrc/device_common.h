@@ -19,12 +19,16 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// FP32 -> BF16 bit pattern, round to nearest even; NaN -> quiet NaN 0x7FC0
-// with the sign kept.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two FP32 values -> two BF16 (round to nearest even) packed lo | hi << 16,
+// with the gfx950 packed conversion.  For every non-NaN input it gives the
+// integer rounding of the bit pattern, (u + 0x7FFF + bit 16 of u) >> 16,
+// overflow to +-Inf included; a NaN stays a NaN.  fp8mot_convert_f32 runs it
+// on any FP32 input so that a test can check it over all 2^32 patterns.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // FP32 -> E4M3FN code with integer round-to-nearest-even on the bit pattern.
@@ -59,7 +63,8 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
 // A byte is 0xFF exactly when its low seven bits plus one carry into bit 7
 // and its own bit 7 is set; the low-seven-bit sums cannot carry across
 // bytes.  Over every FP32 bit pattern, NaN included, this gives the codes of
-// e4m3_encode (checked on the hardware by running both over all 2^32).
+// e4m3_encode (fp8mot_convert_f32 runs both on any FP32 input; a test checks
+// them over all 2^32 patterns).
 __device__ __forceinline__ float clamp448(float v) {
   return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.0f), 448.0f);
 }

@@ -143,16 +143,6 @@ __device__ __forceinline__ void copy_to_lds(v4i rsrc, uint32_t lds_addr, int vof
 }
 
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two FP32 values -> two BF16 (round to nearest even) packed lo | hi << 16,
-// with the gfx950 packed conversion.  For every non-NaN input it gives the
-// bits of the integer rounding in device_common.h (checked on the hardware
-// over all 2^32 patterns); a NaN stays a NaN.
-__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-}
 
 // Lane t of a quad holds byte e = row e of column t; afterwards it holds
 // byte e = column e of row t (a 4x4 byte transpose across the quad).

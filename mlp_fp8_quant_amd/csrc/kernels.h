@@ -53,6 +53,12 @@ hipError_t launch_mfma_ceiling(const uint8_t* a, int64_t na, const uint8_t* b, i
                                int64_t iters, int engine, float* sink, int num_cus,
                                hipStream_t stream);
 
+// Verification aid: out = the kernels' conversion of x [n] (n % 4 == 0, both
+// 16-byte aligned): kind 0 e4m3_pack4 and kind 1 e4m3_encode into n bytes,
+// kind 2 bf16x2_rne into n 16-bit words.
+hipError_t launch_convert_f32(const float* x, void* out, int64_t n, int kind, int max_blocks,
+                              hipStream_t stream);
+
 // u == nullptr: amax of the BF16 tensor x; otherwise amax of silu(x) * u.
 hipError_t launch_observe(const uint16_t* x, const uint16_t* u, int64_t n,
                           fp8mot_observer_state_dev* st, int mode, float c,

@@ -128,6 +128,18 @@ def test_refusals_before_any_device_access():
     assert lib.fp8mot_mfma_ceiling(fake, 64, fake, 63, 1, 1, fake, fl, null) == 1
     assert lib.fp8mot_mfma_ceiling(fake, 64, fake, 64, 0, 0, fake, fl, null) == 1
     assert lib.fp8mot_mfma_ceiling(fake, 64, fake, 64, 1, 2, fake, fl, null) == 1
+    # the conversion verification aid: n < 0 or not a multiple of 4, another
+    # kind, NULL pointers -> INVALID_ARG; n == 0 is a no-op; misaligned ->
+    # MISALIGNED
+    assert lib.fp8mot_convert_f32(fake, fake, -4, 0, null) == 1
+    assert lib.fp8mot_convert_f32(fake, fake, 6, 0, null) == 1
+    assert lib.fp8mot_convert_f32(fake, fake, 8, 3, null) == 1
+    assert lib.fp8mot_convert_f32(fake, fake, 8, -1, null) == 1
+    assert lib.fp8mot_convert_f32(null, fake, 8, 2, null) == 1
+    assert lib.fp8mot_convert_f32(fake, null, 8, 1, null) == 1
+    assert lib.fp8mot_convert_f32(null, null, 0, 0, null) == 0
+    assert lib.fp8mot_convert_f32(odd, fake, 8, 0, null) == 2
+    assert lib.fp8mot_convert_f32(fake, odd, 8, 2, null) == 2
     assert lib.fp8_linear(null, null, null, 0, 4, 16, s, s, 0, null, 0, null) == 0
     # misaligned base pointers -> MISALIGNED
     assert lib.fp8_quant_static(odd, fake, 16, s, null) == 2

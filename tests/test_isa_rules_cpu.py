@@ -103,3 +103,17 @@ def test_mfma_ceiling_loop_keeps_its_mfmas(assembly, engine, mnemonic):
                 found |= n == 8
                 break
     assert found
+
+
+@pytest.mark.parametrize("kind,mnemonic", [(0, "v_cvt_pk_fp8_f32"), (2, "v_cvt_pk_bf16_f32")])
+def test_conversion_aid_runs_the_instructions_the_kernels_use(assembly, kind, mnemonic):
+    """fp8mot_convert_f32 checks the kernels' conversions over all FP32
+    inputs; that holds for the kernels only if its kernel issues the same
+    conversion instruction they do, and the kernels issue it too."""
+    ks = {k: v for k, v in _kernels(assembly["verify.hip"]).items()
+          if "convert_f32_kernel" in k and f"ILi{kind}E" in k}
+    assert len(ks) == 1, list(ks)
+    assert any(l.strip().startswith(mnemonic) for l in next(iter(ks.values())))
+    users = ("elementwise.hip", "gemm.hip") if kind == 0 else ("gemm.hip",)
+    for src in users:
+        assert any(l.strip().startswith(mnemonic) for l in assembly[src]), src
