@@ -154,7 +154,7 @@ int fp8mot_rw_ceiling(const uint16_t* a, const uint16_t* b, uint8_t* out, int64_
  * on given FP8 data with nothing else in the loop (no copies, LDS, decodes or
  * epilogue).  MI355X's clock, and with it the MFMA rate, falls under its
  * power limit by an amount that depends on how much the operand bits toggle,
- * so the GEMM kernels are judged against this rather than the published
+ * so the GEMM kernels are measured against this rather than the published
  * dense peaks alone.  Every wave takes four A fragments from a[0..na) and
  * four B fragments from b[0..nb) (E4M3 codes, each lane its own, indices
  * wrapped), then issues 8 * iters MFMAs on four accumulators:

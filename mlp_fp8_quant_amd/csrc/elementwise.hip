@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void silu_mul_kernel(
 // flight (UN), nontemporal 128-bit accesses and grid as quant_static_kernel /
 // silu_mul_kernel; each output byte is the low byte of the XOR of its input
 // words, so every load is used.  A measurement aid: the quantize and SwiGLU
-// kernels are judged against what the memory system delivers for their mix
+// kernels are measured against what the memory system delivers for their mix
 // (on MI355X these are also the fastest of the unit counts and grid sizes
 // swept for a plain read/write stream of that mix).
 template <int NIN, int UN>
