@@ -357,3 +357,36 @@ def test_nan_codes_propagate(accum, M, N, K):
         check_gemm_fp8_engine(sub[r, c], S[r, c], A[r, c], alpha,
                               fp8_mfma_group_bound(qa[rows[r]], qb[cols[c]]))
     assert np.array_equal(yb[np.ix_(rows, cols)], f32_to_bf16(sub))
+
+
+@pytest.mark.parametrize("sx,sw", [(2.0 ** -70, 2.0 ** -70), (2.0 ** -75, 3 * 2.0 ** -70),
+                                   (2.0 ** 60, 2.0 ** 62)])
+def test_epilogue_alpha_at_the_ends_of_the_fp32_range(sx, sw):
+    """alpha = fp32(s_x * s_w) subnormal, or so large that most outputs
+    overflow.  Subnormal outputs are kept, not flushed to zero: each FP32
+    output is alpha times the sum rounded once onto FP32's subnormal grid,
+    so it may differ from alpha * S by 2^-150 beyond the GEMM bar.  Outputs
+    whose exact value lies beyond FP32's range must be infinities of the
+    sum's sign.  The BF16 output is the RNE of the FP32 output either way."""
+    dev = device()
+    print(f"alpha case sx={sx!r} sw={sw!r}", flush=True)
+    rng = np.random.default_rng(abs(int(np.log2(sx))) * 131 + abs(int(np.log2(sw))))
+    M, N, K = 96, 80, 256
+    qa, qb = _codes(rng, (M, K)), _codes(rng, (N, K))
+    out = _run(qa, qb, np.float32(sx), np.float32(sw), dev)
+    y32f = host_f32(out[fp8.OUT_F32])
+    y32 = y32f.astype(np.float64)
+    S, A = olin.gemm_exact(qa, qb)
+    alpha = float(olin.epilogue_alpha(np.float32(sx), np.float32(sw)))
+    exact = alpha * S
+    fmax = float(np.finfo(np.float32).max)
+    big = np.abs(exact) > fmax * (1 + 1e-4)
+    fin = np.abs(exact) + 1e-5 * alpha * A < fmax
+    assert np.all(np.isinf(y32[big]) & (np.sign(y32[big]) == np.sign(exact[big])))
+    assert np.all(np.abs(y32[fin] - exact[fin]) <= 1e-5 * alpha * A[fin] + 2.0 ** -150)
+    assert np.array_equal(host_bits(out[fp8.OUT_BF16]), f32_to_bf16(y32f))
+    if alpha < 2.0 ** -126:
+        sub = (y32 != 0) & (np.abs(y32) < 2.0 ** -126)
+        assert np.count_nonzero(sub) > (M * N // 2 if alpha < 2.0 ** -140 else M * N // 20)
+    else:
+        assert np.count_nonzero(big) > M * N // 4
